@@ -1,0 +1,54 @@
+"""The quotient scheme of the quantisation kernels, checked exhaustively on the CPU.
+
+The kernels divide each element by its block scale s as
+    q = RN(x * r),  t = RN(q * s - x) (one fma),  result = RN(q - t * r) (one fma)
+with r = RN(1 / s).  This test emulates those three roundings with exact
+rational arithmetic and compares the result with the correctly rounded
+quotient RN(x / s) that act_quant requires, for every pair of significands the
+kernels can meet: x any bf16 significand (128), s any significand of
+RN(max(amax, fl(1e-4)) / 448) with amax a bf16 value (128, plus the clamp
+value), both signs and several relative binades.  Rounding of all three steps
+is invariant under scaling x and s by powers of two while every intermediate
+stays normal, which holds whenever the quotient is large enough (>= 2^-11) to
+round to a non-zero e4m3 code; smaller quotients encode to a signed zero
+either way.  For ue8m0 scales (powers of two) every step is exact.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+
+def rn32(x):
+    if x == 0:
+        return Fraction(0)
+    neg = x < 0
+    a = -x if neg else x
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:
+        E -= 1
+    sp = Fraction(2) ** (E - 23)
+    q = a / sp
+    lo = q.numerator // q.denominator
+    rem = q - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2):
+        lo += 1
+    return -(lo * sp) if neg else lo * sp
+
+
+def test_corrected_quotient_is_correctly_rounded():
+    scales = {rn32(Fraction(128 + m, 128) / 448) for m in range(128)}
+    scales.add(rn32(Fraction(float(np.float32(1e-4))) / 448))
+    bad = []
+    for s in scales:
+        r = rn32(1 / s)
+        for m in range(128):
+            for sh in (-8, 0, 1, 5, 11):
+                x = Fraction(128 + m, 128) * Fraction(2) ** (-sh)
+                for xx in (x, -x):
+                    q = rn32(xx * r)
+                    t = rn32(q * s - xx)
+                    q1 = rn32(q - t * r)
+                    if q1 != rn32(xx / s):
+                        bad.append((s, xx))
+    assert not bad, bad[:5]
