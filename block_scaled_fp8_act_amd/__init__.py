@@ -1,0 +1,185 @@
+"""dsfp8: block-scaled FP8 linear layer for AMD MI355X (gfx950).
+
+Python binding of libdsfp8.so.  Each function checks tensor placement and
+dtypes, allocates its outputs with torch on the input's device, and calls the
+C entry point of the same name on torch's current stream; every step of the
+computation runs in the library's HIP kernels.  e4m3 tensors are exchanged as
+``torch.uint8`` (``torch.float8_e4m3fn`` inputs are accepted and viewed as
+bytes).  Scales are ``torch.float32``.
+
+The operations follow the DeepSeek-V3 inference kernels as described in the
+"DeepSeek-V3 Administrator & Developer Guide" (sections 6.3, 6.4, 8.5) and the
+DocSearch index of the DeepSeek-V3 README (item 3, weight_scale_inv); see
+include/dsfp8.h for the exact contracts.
+"""
+
+import torch
+
+from . import _lib
+
+BLOCK = 128
+_SCALE_FMT = {"fp32": 0, "ue8m0": 1}
+
+
+class Dsfp8Error(ValueError):
+    """A libdsfp8 call rejected its arguments or failed to launch."""
+
+
+def kblocks(n):
+    return (int(n) + BLOCK - 1) // BLOCK
+
+
+def status_string(st):
+    return _lib.load().dsfp8_status_string(int(st)).decode()
+
+
+def abi_version():
+    return _lib.load().dsfp8_abi_version()
+
+
+def _check(name, st):
+    if st != 0:
+        raise Dsfp8Error(f"{name}: {status_string(st)} (status {st})")
+
+
+def _fmt(scale_fmt):
+    if scale_fmt not in _SCALE_FMT:
+        raise Dsfp8Error(f"scale_fmt must be one of {sorted(_SCALE_FMT)}, got {scale_fmt!r}")
+    return _SCALE_FMT[scale_fmt]
+
+
+def _bytes(t):
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _mat(t, name, dtypes, dim=2):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise Dsfp8Error(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise Dsfp8Error(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.dim() != dim:
+        raise Dsfp8Error(f"Input tensors must have {dim} dimensions ({name} has {t.dim()})")
+    if t.numel() > 0 and t.stride(-1) != 1:
+        raise Dsfp8Error(f"Input tensor must be contiguous in its last dimension ({name})")
+    return t
+
+
+def _ld(t):
+    return t.stride(-2) if t.numel() > 0 else t.shape[-1]
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def act_quant(x, scale_fmt="fp32"):
+    """Quantise bf16 ``x [M, K]`` per row and per 128 columns.
+
+    Returns ``(y uint8 [M, K], s float32 [M, ceil(K/128)])`` with x ~= e4m3(y) * s.
+    """
+    _mat(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    y = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, kblocks(K)), dtype=torch.float32, device=x.device)
+    st = _lib.load().dsfp8_act_quant(x.data_ptr(), M, K, _ld(x), y.data_ptr(), K, s.data_ptr(), kblocks(K),
+                                     _fmt(scale_fmt), _stream(x))
+    _check("act_quant", st)
+    return y, s
+
+
+def silu_mul_act_quant(g, u, scale_fmt="fp32", return_h=False):
+    """``act_quant(bf16(SiLU(g) * u))`` in one pass; optionally also return h."""
+    _mat(g, "g", (torch.bfloat16,))
+    _mat(u, "u", (torch.bfloat16,))
+    if g.shape != u.shape:
+        raise Dsfp8Error(f"g and u must have the same shape, got {tuple(g.shape)} and {tuple(u.shape)}")
+    M, I = g.shape
+    y = torch.empty((M, I), dtype=torch.uint8, device=g.device)
+    s = torch.empty((M, kblocks(I)), dtype=torch.float32, device=g.device)
+    h = torch.empty((M, I), dtype=torch.bfloat16, device=g.device) if return_h else None
+    st = _lib.load().dsfp8_silu_mul_act_quant(
+        g.data_ptr(), _ld(g), u.data_ptr(), _ld(u), M, I, y.data_ptr(), I, s.data_ptr(), kblocks(I),
+        h.data_ptr() if h is not None else None, I, _fmt(scale_fmt), _stream(g))
+    _check("silu_mul_act_quant", st)
+    return (y, s, h) if return_h else (y, s)
+
+
+def weight_quant(w, scale_fmt="fp32"):
+    """Quantise fp32 or bf16 weights ``[N, K]`` to e4m3 with 128x128 fp32 block scales."""
+    _mat(w, "w", (torch.float32, torch.bfloat16))
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    S = torch.empty((kblocks(N), kblocks(K)), dtype=torch.float32, device=w.device)
+    dtype = 0 if w.dtype == torch.float32 else 1
+    st = _lib.load().dsfp8_weight_quant(w.data_ptr(), dtype, N, K, _ld(w), q.data_ptr(), K, S.data_ptr(),
+                                        kblocks(K), _fmt(scale_fmt), _stream(w))
+    _check("weight_quant", st)
+    return q, S
+
+
+def weight_dequant(q, S):
+    """bf16 ``[N, K]`` = e4m3 ``q`` times its 128x128 block scale ``S``."""
+    q = _mat(_bytes(q), "w", (torch.uint8,))
+    _mat(S, "s", (torch.float32,))
+    N, K = q.shape
+    if tuple(S.shape) != (kblocks(N), kblocks(K)):
+        raise Dsfp8Error(f"scale grid must be {(kblocks(N), kblocks(K))}, got {tuple(S.shape)}")
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=q.device)
+    st = _lib.load().dsfp8_weight_dequant(q.data_ptr(), N, K, _ld(q), S.data_ptr(), _ld(S), out.data_ptr(), K,
+                                          _stream(q))
+    _check("weight_dequant", st)
+    return out
+
+
+def gemm(a, a_s, b, b_s):
+    """bf16 ``C [M, N] = A W^T`` with per-K-block scales (A e4m3 [M,K], W e4m3 [N,K])."""
+    a = _mat(_bytes(a), "a", (torch.uint8,))
+    b = _mat(_bytes(b), "b", (torch.uint8,))
+    _mat(a_s, "a_s", (torch.float32,))
+    _mat(b_s, "b_s", (torch.float32,))
+    M, K = a.shape
+    N, K2 = b.shape
+    if K2 != K:
+        raise Dsfp8Error(f"a and b disagree on K: {K} vs {K2}")
+    if tuple(a_s.shape) != (M, kblocks(K)) or tuple(b_s.shape) != (kblocks(N), kblocks(K)):
+        raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and b_s [ceil(N/128), ceil(K/128)]")
+    lib = _lib.load()
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    wsb = lib.dsfp8_gemm_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device) if wsb else None
+    st = lib.dsfp8_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), _ld(a_s), b.data_ptr(), _ld(b), b_s.data_ptr(),
+                        _ld(b_s), c.data_ptr(), N, M, N, K, ws.data_ptr() if ws is not None else None, wsb,
+                        _stream(a))
+    _check("gemm", st)
+    return c
+
+
+def grouped_gemm(a, a_s, b, b_s, offsets):
+    """Per-expert product over row ranges: rows ``offsets[e]:offsets[e+1]`` of A use W[e].
+
+    ``b`` is e4m3 ``[E, N, K]``, ``b_s`` fp32 ``[E, ceil(N/128), ceil(K/128)]``,
+    ``offsets`` int32 ``[E+1]`` on the device.  Returns bf16 ``[M_total, N]``.
+    """
+    a = _mat(_bytes(a), "a", (torch.uint8,))
+    b = _mat(_bytes(b), "b", (torch.uint8,), dim=3)
+    _mat(a_s, "a_s", (torch.float32,))
+    _mat(b_s, "b_s", (torch.float32,), dim=3)
+    if not offsets.is_cuda or offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise Dsfp8Error("offsets must be a contiguous int32 CUDA tensor of length E+1")
+    M, K = a.shape
+    E, N, K2 = b.shape
+    if K2 != K or offsets.numel() != E + 1:
+        raise Dsfp8Error("shape mismatch between a, b and offsets")
+    if not b.is_contiguous() or not b_s.is_contiguous():
+        raise Dsfp8Error("Input tensor must be contiguous (b, b_s)")
+    if tuple(b_s.shape) != (E, kblocks(N), kblocks(K)) or tuple(a_s.shape) != (M, kblocks(K)):
+        raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and b_s [E, ceil(N/128), ceil(K/128)]")
+    lib = _lib.load()
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    wsb = lib.dsfp8_grouped_gemm_workspace_bytes(E, M, N, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+    st = lib.dsfp8_grouped_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), _ld(a_s), b.data_ptr(), K, b_s.data_ptr(),
+                                kblocks(K), offsets.data_ptr(), E, M, N, K, c.data_ptr(), N, ws.data_ptr(), wsb,
+                                _stream(a))
+    _check("grouped_gemm", st)
+    return c

@@ -1,0 +1,252 @@
+// C ABI of libdsfp8: argument validation (plain host code, no HIP call before
+// every check has passed) and dispatch to the kernel launchers.
+#include <atomic>
+
+#include "../../include/dsfp8.h"
+#include "launch.h"
+
+namespace dsfp8 {
+
+int device_cu_count() {
+  // Read-only cache of a device attribute; a race only repeats the query.
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace dsfp8
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows, columns and K below 2^31
+constexpr int64_t kMaxExperts = 65536;
+
+inline int64_t nblk(int64_t n) { return (n + DSFP8_BLOCK - 1) / DSFP8_BLOCK; }
+inline bool al(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+inline bool dim_ok(int64_t v) { return v >= 0 && v < kMaxDim; }
+
+// A matrix argument: rows x cols elements with row stride ld.
+inline dsfp8_status check_mat(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t elt) {
+  if (ld < cols || ld < 0 || ld >= ((int64_t)1 << 40)) return DSFP8_ERR_LD;
+  if (rows > 0 && cols > 0 && p == nullptr) return DSFP8_ERR_NULL;
+  if (p != nullptr && !al(p, elt)) return DSFP8_ERR_ALIGN;
+  return DSFP8_OK;
+}
+
+#define DSFP8_TRY(expr)              \
+  do {                               \
+    const dsfp8_status st_ = (expr); \
+    if (st_ != DSFP8_OK) return st_; \
+  } while (0)
+
+inline dsfp8_status launched(hipError_t e) { return e == hipSuccess ? DSFP8_OK : DSFP8_ERR_LAUNCH; }
+
+dsfp8_status check_quant_out(int64_t M, int64_t K, void* y, int64_t ldy, float* s, int64_t lds) {
+  DSFP8_TRY(check_mat(y, M, K, ldy, 1));
+  DSFP8_TRY(check_mat(s, M, nblk(K), lds, 4));
+  return DSFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsfp8_abi_version(void) { return DSFP8_ABI_VERSION; }
+
+const char* dsfp8_status_string(dsfp8_status st) {
+  switch (st) {
+    case DSFP8_OK: return "ok";
+    case DSFP8_ERR_NULL: return "a required pointer is NULL";
+    case DSFP8_ERR_SHAPE: return "a size is negative or outside the supported range";
+    case DSFP8_ERR_LD: return "a leading dimension is smaller than its row length";
+    case DSFP8_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case DSFP8_ERR_SCALE_FMT: return "unknown scale format";
+    case DSFP8_ERR_WORKSPACE: return "workspace is smaller than required";
+    case DSFP8_ERR_LAUNCH: return "the HIP runtime reported a launch failure";
+    case DSFP8_ERR_DTYPE: return "unknown element type";
+    default: return "unknown status";
+  }
+}
+
+dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, void* y, int64_t ldy, float* s,
+                             int64_t lds, int scale_fmt, hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
+  DSFP8_TRY(check_mat(x, M, K, ldx, 2));
+  DSFP8_TRY(check_quant_out(M, K, y, ldy, s, lds));
+  dsfp8::ActQuantArgs a{};
+  a.g = static_cast<const uint16_t*>(x);
+  a.ldg = ldx;
+  a.u = nullptr;
+  a.ldu = 0;
+  a.M = M;
+  a.K = K;
+  a.y = static_cast<uint8_t*>(y);
+  a.ldy = ldy;
+  a.s = s;
+  a.lds = lds;
+  a.h = nullptr;
+  a.ldh = 0;
+  a.ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
+  return launched(dsfp8::launch_act_quant(a, stream));
+}
+
+dsfp8_status dsfp8_silu_mul_act_quant(const void* g, int64_t ldg, const void* u, int64_t ldu, int64_t M, int64_t I,
+                                      void* y, int64_t ldy, float* s, int64_t lds, void* h, int64_t ldh,
+                                      int scale_fmt, hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(I)) return DSFP8_ERR_SHAPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
+  DSFP8_TRY(check_mat(g, M, I, ldg, 2));
+  DSFP8_TRY(check_mat(u, M, I, ldu, 2));
+  DSFP8_TRY(check_quant_out(M, I, y, ldy, s, lds));
+  if (h != nullptr) DSFP8_TRY(check_mat(h, M, I, ldh, 2));
+  dsfp8::ActQuantArgs a{};
+  a.g = static_cast<const uint16_t*>(g);
+  a.ldg = ldg;
+  a.u = static_cast<const uint16_t*>(u);
+  a.ldu = ldu;
+  a.M = M;
+  a.K = I;
+  a.y = static_cast<uint8_t*>(y);
+  a.ldy = ldy;
+  a.s = s;
+  a.lds = lds;
+  a.h = static_cast<uint16_t*>(h);
+  a.ldh = h ? ldh : 0;
+  a.ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
+  // The fused path needs a non-null u to select SiLU gating; an empty problem
+  // launches nothing anyway.
+  if (M == 0 || I == 0) return DSFP8_OK;
+  return launched(dsfp8::launch_act_quant(a, stream));
+}
+
+dsfp8_status dsfp8_weight_quant(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw, void* q, int64_t ldq,
+                                float* S, int64_t ldS, int scale_fmt, hipStream_t stream) {
+  if (!dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  if (dtype != DSFP8_DTYPE_F32 && dtype != DSFP8_DTYPE_BF16) return DSFP8_ERR_DTYPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
+  DSFP8_TRY(check_mat(w, N, K, ldw, dtype == DSFP8_DTYPE_F32 ? 4 : 2));
+  DSFP8_TRY(check_mat(q, N, K, ldq, 1));
+  DSFP8_TRY(check_mat(S, nblk(N), nblk(K), ldS, 4));
+  dsfp8::WeightQuantArgs a{};
+  a.w = w;
+  a.bf16_in = dtype == DSFP8_DTYPE_BF16;
+  a.N = N;
+  a.K = K;
+  a.ldw = ldw;
+  a.q = static_cast<uint8_t*>(q);
+  a.ldq = ldq;
+  a.S = S;
+  a.ldS = ldS;
+  a.ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
+  return launched(dsfp8::launch_weight_quant(a, stream));
+}
+
+dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t ldw, const float* S, int64_t ldS,
+                                  void* out, int64_t ldo, hipStream_t stream) {
+  if (!dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  DSFP8_TRY(check_mat(w, N, K, ldw, 1));
+  DSFP8_TRY(check_mat(S, nblk(N), nblk(K), ldS, 4));
+  DSFP8_TRY(check_mat(out, N, K, ldo, 2));
+  dsfp8::DequantArgs a{};
+  a.w = static_cast<const uint8_t*>(w);
+  a.N = N;
+  a.K = K;
+  a.ldw = ldw;
+  a.S = S;
+  a.ldS = ldS;
+  a.out = static_cast<uint16_t*>(out);
+  a.ldo = ldo;
+  return launched(dsfp8::launch_weight_dequant(a, stream));
+}
+
+size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas, const void* B, int64_t ldb,
+                        const float* b_s, int64_t ldbs, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  DSFP8_TRY(check_mat(A, M, K, lda, 1));
+  DSFP8_TRY(check_mat(a_s, M, nblk(K), ldas, 4));
+  DSFP8_TRY(check_mat(B, N, K, ldb, 1));
+  DSFP8_TRY(check_mat(b_s, nblk(N), nblk(K), ldbs, 4));
+  DSFP8_TRY(check_mat(C, M, N, ldc, 2));
+  if (workspace_bytes < dsfp8_gemm_workspace_bytes(M, N, K)) return DSFP8_ERR_WORKSPACE;
+  (void)workspace;
+  dsfp8::GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.lda = lda;
+  a.a_s = a_s;
+  a.ldas = ldas;
+  a.B = static_cast<const uint8_t*>(B);
+  a.ldb = ldb;
+  a.b_s = b_s;
+  a.ldbs = ldbs;
+  a.C = static_cast<uint16_t*>(C);
+  a.ldc = ldc;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return launched(dsfp8::launch_gemm(a, stream));
+}
+
+size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K) {
+  (void)M_total;
+  (void)N;
+  (void)K;
+  if (E < 1 || E > kMaxExperts) return 0;
+  return dsfp8::grouped_workspace_bytes(E);
+}
+
+dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas, const void* B,
+                                int64_t ldb, const float* b_s, int64_t ldbs, const int32_t* offsets, int64_t E,
+                                int64_t M_total, int64_t N, int64_t K, void* C, int64_t ldc, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!dim_ok(M_total) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
+  if (offsets == nullptr) return DSFP8_ERR_NULL;
+  if (!al(offsets, 4)) return DSFP8_ERR_ALIGN;
+  DSFP8_TRY(check_mat(A, M_total, K, lda, 1));
+  DSFP8_TRY(check_mat(a_s, M_total, nblk(K), ldas, 4));
+  // Every expert's weight must exist even when no row is routed to it.
+  DSFP8_TRY(check_mat(B, E * N, K, ldb, 1));
+  DSFP8_TRY(check_mat(b_s, E * nblk(N), nblk(K), ldbs, 4));
+  DSFP8_TRY(check_mat(C, M_total, N, ldc, 2));
+  const size_t need = dsfp8_grouped_gemm_workspace_bytes(E, M_total, N, K);
+  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
+  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
+  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
+  dsfp8::GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.lda = lda;
+  a.a_s = a_s;
+  a.ldas = ldas;
+  a.B = static_cast<const uint8_t*>(B);
+  a.ldb = ldb;
+  a.b_s = b_s;
+  a.ldbs = ldbs;
+  a.C = static_cast<uint16_t*>(C);
+  a.ldc = ldc;
+  a.M = M_total;
+  a.N = N;
+  a.K = K;
+  a.offsets = offsets;
+  a.E = E;
+  a.tile_start = static_cast<int32_t*>(workspace);
+  return launched(dsfp8::launch_grouped_gemm(a, stream));
+}
+
+}  // extern "C"

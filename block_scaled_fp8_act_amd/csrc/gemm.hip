@@ -1,0 +1,404 @@
+// Block-scaled FP8 products on gfx950 MFMA: dense and grouped over per-expert
+// row ranges.
+//
+// The product ("DeepSeek-V3 Administrator & Developer Guide", 8.5.3) adds,
+// for every 128-wide K-block b, the block's partial dot product multiplied by
+// the activation scale a_s[m, b] and the weight scale b_s[n/128, b].  On CDNA4
+// one v_mfma_f32_16x16x128_f8f6f4 consumes exactly one K-block of a 16x16
+// output tile, so each K-block's partial product comes out of a single MFMA
+// (started from zero) and is folded into the fp32 accumulator with one VALU
+// fma per output element, using the per-row product a_s * b_s.  A workgroup
+// stages BM x 128 bytes of A and BN x 128 bytes of B per K-block in LDS
+// (double-buffered, 16-byte chunks XOR-swizzled by row so that the fragment
+// reads of eight consecutive rows hit distinct banks), together with the BM
+// activation scales of that K-block.  Global loads for K-block b+1 are issued
+// before the MFMAs of block b, so their latency overlaps the math.
+//
+// Workgroups are mapped to tiles so that each XCD (workgroup i runs on XCD
+// i % 8) owns a contiguous range of tiles, ordered in groups of GROUP_M tile
+// rows, which keeps the A and B panels in use on one XCD inside its L2.
+#include "device.h"
+#include "launch.h"
+
+namespace dsfp8 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 128;
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int kRowsPerPass = kThreads / 8;  // 8 threads load one 128-byte row
+  static constexpr int A_CHUNKS = BM / kRowsPerPass;
+  static constexpr int B_CHUNKS = BN / kRowsPerPass;
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  static constexpr int CPAD = 8;                     // bf16 elements of padding per staged C row
+  static constexpr int C_BYTES = WAVES_M * WAVES_N * WM * (WN + CPAD) * 2;
+  static constexpr int MAIN_BYTES = 2 * (A_BYTES + B_BYTES) + 2 * BM * 4;
+  static constexpr int LDS_BYTES = MAIN_BYTES > C_BYTES ? MAIN_BYTES : C_BYTES;
+  static_assert(BM % kRowsPerPass == 0 && BN % kRowsPerPass == 0, "tile rows");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-block");
+  static_assert(BM <= kThreads, "one thread per activation scale");
+};
+
+using Cfg128 = Cfg<128, 128, 2, 2>;
+
+// 16 bytes of one row starting at column k (a multiple of 16); bytes at
+// columns >= K, or of a row outside the matrix, read as zero.  VEC is the
+// widest access the host proved aligned; it divides K, so each VEC-wide piece
+// is entirely inside or entirely outside the row.
+template <int VEC>
+__device__ __forceinline__ u32x4 load_chunk(const uint8_t* row, int64_t k, int64_t K, bool row_ok) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (!row_ok) return v;
+  if constexpr (VEC == 16) {
+    if (k < K) v = *reinterpret_cast<const u32x4*>(row + k);
+  } else if constexpr (VEC == 8) {
+    if (k < K) { u32x2 t = *reinterpret_cast<const u32x2*>(row + k); v.x = t.x; v.y = t.y; }
+    if (k + 8 < K) { u32x2 t = *reinterpret_cast<const u32x2*>(row + k + 8); v.z = t.x; v.w = t.y; }
+  } else if constexpr (VEC == 4) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(row + k);
+    if (k < K) v.x = p[0];
+    if (k + 4 < K) v.y = p[1];
+    if (k + 8 < K) v.z = p[2];
+    if (k + 12 < K) v.w = p[3];
+  } else {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (k + i < K) w[i >> 2] |= (uint32_t)row[k + i] << (8 * (i & 3));
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+  }
+  return v;
+}
+
+// Byte offset of 16-byte chunk c of tile row r in LDS.
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
+
+// MFMA operand of one 16-row slice: lane (r, g) = (lane % 16, lane / 16) holds
+// K bytes [32g, 32g + 32) of row r.  A and B use the same K assignment, so the
+// dot product over the K-block does not depend on the order in which the
+// matrix core consumes the bytes.
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int g) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * g));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * g + 1));
+  v8i f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+struct TileRef {
+  const uint8_t* A;      // matrix base (absolute rows)
+  const float* a_s;
+  const uint8_t* B;      // this tile's weight [N, K]
+  const float* b_s;      // this tile's weight scales
+  int64_t row0, row_end; // rows [row0, min(row0 + BM, row_end)) are computed
+  int64_t n0;
+};
+
+template <class CF, int VEC>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
+  constexpr int BM = CF::BM;
+  uint8_t* As = smem;
+  uint8_t* Bs = smem + 2 * CF::A_BYTES;
+  float* Ss = reinterpret_cast<float*>(smem + 2 * (CF::A_BYTES + CF::B_BYTES));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int64_t K = p.K, N = p.N;
+  const int nkb = (int)((K + BK - 1) / BK);
+  const int64_t kbn = (N + BK - 1) / BK;
+
+  const int ck = tid & 7;
+  const int rbase = tid >> 3;
+
+  u32x4 ra[CF::A_CHUNKS], rb[CF::B_CHUNKS];
+  float rs = 0.0f;
+
+  auto gload = [&](int kb) {
+    const int64_t k = (int64_t)kb * BK + ck * 16;
+#pragma unroll
+    for (int i = 0; i < CF::A_CHUNKS; ++i) {
+      const int64_t row = t.row0 + rbase + i * CF::kRowsPerPass;
+      const bool ok = row < t.row_end;
+      ra[i] = load_chunk<VEC>(t.A + (ok ? row : 0) * p.lda, k, K, ok);
+    }
+#pragma unroll
+    for (int i = 0; i < CF::B_CHUNKS; ++i) {
+      const int64_t n = t.n0 + rbase + i * CF::kRowsPerPass;
+      const bool ok = n < N;
+      rb[i] = load_chunk<VEC>(t.B + (ok ? n : 0) * p.ldb, k, K, ok);
+    }
+    if (tid < BM) {
+      const int64_t row = t.row0 + tid;
+      rs = row < t.row_end ? t.a_s[row * p.ldas + kb] : 0.0f;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CF::A_CHUNKS; ++i)
+      *reinterpret_cast<u32x4*>(As + buf * CF::A_BYTES + swz(rbase + i * CF::kRowsPerPass, ck)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < CF::B_CHUNKS; ++i)
+      *reinterpret_cast<u32x4*>(Bs + buf * CF::B_BYTES + swz(rbase + i * CF::kRowsPerPass, ck)) = rb[i];
+    if (tid < BM) Ss[buf * BM + tid] = rs;
+  };
+
+  v4f acc[CF::TM][CF::TN];
+#pragma unroll
+  for (int i = 0; i < CF::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The weight scale row of this wave's 128-column block (clamped for waves
+  // past the last column, whose results are never stored).
+  int64_t nbi = (t.n0 + wn * CF::WN) / BK;
+  if (nbi > kbn - 1) nbi = kbn - 1;
+  const float* bsrow = t.b_s + nbi * p.ldbs;
+
+  if (nkb > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int fr = lane & 15, fg = lane >> 4;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) gload(kb + 1);
+    const float bsv = bsrow[kb];
+    const uint8_t* at = As + buf * CF::A_BYTES;
+    const uint8_t* bt = Bs + buf * CF::B_BYTES;
+    v8i bfr[CF::TN];
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j) bfr[j] = read_frag(bt, wn * CF::WN + j * 16 + fr, fg);
+#pragma unroll
+    for (int i = 0; i < CF::TM; ++i) {
+      const v8i afr = read_frag(at, wm * CF::WM + i * 16 + fr, fg);
+      const v4f sa = *reinterpret_cast<const v4f*>(Ss + buf * BM + wm * CF::WM + i * 16 + 4 * fg);
+      const v4f sc = sa * bsv;
+#pragma unroll
+      for (int j = 0; j < CF::TN; ++j) {
+        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc[v], acc[i][j][v]);
+      }
+    }
+    if (kb + 1 < nkb) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: round to bf16, stage this wave's WM x WN tile in LDS, then write
+  // rows of C with 16-byte stores.
+  constexpr int CS = CF::WN + CF::CPAD;
+  uint16_t* cst = reinterpret_cast<uint16_t*>(smem) + wave * CF::WM * CS;
+#pragma unroll
+  for (int i = 0; i < CF::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const __bf16 h = (__bf16)acc[i][j][v];
+        cst[(i * 16 + 4 * fg + v) * CS + j * 16 + fr] = __builtin_bit_cast(uint16_t, h);
+      }
+  __syncthreads();
+  const int64_t crow0 = t.row0 + wm * CF::WM;
+  const int64_t ccol0 = t.n0 + wn * CF::WN;
+  const int64_t row_lim = t.row_end;
+  const bool cvec = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 8 == 0);
+  constexpr int CPR = CF::WN / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int it = 0; it < CF::WM * CPR / 64; ++it) {
+    const int c = lane + 64 * it;
+    const int r = c / CPR, cc = c % CPR;
+    const int64_t row = crow0 + r;
+    const int64_t col = ccol0 + cc * 8;
+    if (row >= row_lim || col >= N) continue;
+    const uint16_t* src = cst + r * CS + cc * 8;
+    uint16_t* dst = p.C + row * p.ldc + col;
+    if (cvec && col + 8 <= N) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = src[e];
+    }
+  }
+}
+
+// Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges, then
+// GROUP_M-row groups inside a range.
+__device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  const int64_t total = tiles_m * tiles_n;
+  const int64_t q = total / kXcds, r = total % kXcds;
+  const int64_t xcd = pid % kXcds, idx = pid / kXcds;
+  pid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  const int64_t per_group = (int64_t)kGroupM * tiles_n;
+  const int64_t gid = pid / per_group;
+  const int64_t first_m = gid * kGroupM;
+  const int64_t gsize = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int64_t in = pid % per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+template <class CF, int VEC>
+__global__ __launch_bounds__(CF::kThreads) void gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
+  const int64_t tiles_m = (p.M + CF::BM - 1) / CF::BM;
+  const int64_t tiles_n = (p.N + CF::BN - 1) / CF::BN;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  TileRef t;
+  t.A = p.A;
+  t.a_s = p.a_s;
+  t.B = p.B;
+  t.b_s = p.b_s;
+  t.row0 = tm * CF::BM;
+  t.row_end = p.M;
+  t.n0 = tn * CF::BN;
+  gemm_tile<CF, VEC>(p, t, smem);
+}
+
+// Expert row range [lo, hi) with every bound clamped into [0, M_total].
+__device__ __forceinline__ void expert_rows(const int32_t* offsets, int64_t e, int64_t M, int64_t& lo, int64_t& hi) {
+  int64_t a = offsets[e], b = offsets[e + 1];
+  a = a < 0 ? 0 : (a > M ? M : a);
+  b = b < a ? a : (b > M ? M : b);
+  lo = a;
+  hi = b;
+}
+
+// tile_start[e] = number of BM-row tiles of experts 0..e-1 (one workgroup).
+__global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* offsets, int64_t E, int64_t M, int bm,
+                                                             int32_t* tile_start) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    carry = 0;
+    tile_start[0] = 0;
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < E; base += 1024) {
+    const int64_t e = base + t;
+    int32_t cnt = 0;
+    if (e < E) {
+      int64_t lo, hi;
+      expert_rows(offsets, e, M, lo, hi);
+      cnt = (int32_t)((hi - lo + bm - 1) / bm);
+    }
+    part[t] = cnt;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int32_t add = t >= d ? part[t - d] : 0;
+      __syncthreads();
+      part[t] += add;
+      __syncthreads();
+    }
+    if (e < E) tile_start[e + 1] = carry + part[t];
+    __syncthreads();
+    if (t == 1023) carry += part[1023];
+    __syncthreads();
+  }
+}
+
+template <class CF, int VEC>
+__global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
+  const int64_t slot = blockIdx.x;
+  const int32_t* ts = p.tile_start;
+  if (slot >= ts[p.E]) return;
+  // Last expert e with ts[e] <= slot; then ts[e+1] > slot.
+  int64_t lo = 0, hi = p.E;  // invariant: ts[lo] <= slot < ts[hi]
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (ts[mid] <= slot) lo = mid;
+    else hi = mid;
+  }
+  const int64_t e = lo;
+  int64_t r0, r1;
+  expert_rows(p.offsets, e, p.M, r0, r1);
+  const int64_t kbn = (p.N + BK - 1) / BK;
+  const int64_t kbk = (p.K + BK - 1) / BK;
+  TileRef t;
+  t.A = p.A;
+  t.a_s = p.a_s;
+  t.B = p.B + e * p.N * p.ldb;
+  t.b_s = p.b_s + e * kbn * p.ldbs;
+  (void)kbk;
+  t.row0 = r0 + (slot - ts[e]) * CF::BM;
+  t.row_end = r1;
+  t.n0 = (int64_t)blockIdx.y * CF::BN;
+  gemm_tile<CF, VEC>(p, t, smem);
+}
+
+inline bool aligned(const void* q, size_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; }
+
+// Widest load width (bytes) valid for every row start of A and B and for K.
+int pick_vec(const GemmArgs& a) {
+  const int cands[3] = {16, 8, 4};
+  for (int v : cands)
+    if (a.K % v == 0 && a.lda % v == 0 && a.ldb % v == 0 && aligned(a.A, v) && aligned(a.B, v)) return v;
+  return 1;
+}
+
+template <class CF>
+hipError_t launch_dense(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = ((a.M + CF::BM - 1) / CF::BM) * ((a.N + CF::BN - 1) / CF::BN);
+  dim3 g((unsigned)tiles), b(CF::kThreads);
+  switch (pick_vec(a)) {
+    case 16: hipLaunchKernelGGL((gemm_kernel<CF, 16>), g, b, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemm_kernel<CF, 8>), g, b, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<CF, 4>), g, b, 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_kernel<CF, 1>), g, b, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <class CF>
+hipError_t launch_grouped(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.M, CF::BM, a.tile_start);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t slots = (a.M + CF::BM - 1) / CF::BM + a.E;
+  dim3 g((unsigned)slots, (unsigned)((a.N + CF::BN - 1) / CF::BN)), b(CF::kThreads);
+  switch (pick_vec(a)) {
+    case 16: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 16>), g, b, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 8>), g, b, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 4>), g, b, 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 1>), g, b, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  return launch_dense<Cfg128>(a, stream);
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
+  if (a.N == 0 || a.M == 0) return hipSuccess;
+  return launch_grouped<Cfg128>(a, stream);
+}
+
+size_t grouped_workspace_bytes(int64_t E) {
+  const size_t n = (size_t)(E + 1) * sizeof(int32_t);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace dsfp8

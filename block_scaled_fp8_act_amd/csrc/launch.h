@@ -1,0 +1,75 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsfp8 {
+
+struct ActQuantArgs {
+  const uint16_t* g;  // bf16 input (the SiLU gate input when u != nullptr)
+  int64_t ldg;
+  const uint16_t* u;  // bf16 up-projection input, or nullptr for plain act_quant
+  int64_t ldu;
+  int64_t M, K;
+  uint8_t* y;
+  int64_t ldy;
+  float* s;
+  int64_t lds;
+  uint16_t* h;        // optional bf16 output of SiLU(g)*u
+  int64_t ldh;
+  bool ue8m0;
+};
+
+struct WeightQuantArgs {
+  const void* w;
+  bool bf16_in;
+  int64_t N, K, ldw;
+  uint8_t* q;
+  int64_t ldq;
+  float* S;
+  int64_t ldS;
+  bool ue8m0;
+};
+
+struct DequantArgs {
+  const uint8_t* w;
+  int64_t N, K, ldw;
+  const float* S;
+  int64_t ldS;
+  uint16_t* out;
+  int64_t ldo;
+};
+
+struct GemmArgs {
+  const uint8_t* A;
+  int64_t lda;
+  const float* a_s;
+  int64_t ldas;
+  const uint8_t* B;
+  int64_t ldb;
+  const float* b_s;
+  int64_t ldbs;
+  uint16_t* C;
+  int64_t ldc;
+  int64_t M, N, K;
+  // grouped form only
+  const int32_t* offsets;
+  int64_t E;
+  int32_t* tile_start;  // workspace: E+1 ints
+};
+
+hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream);
+hipError_t launch_weight_quant(const WeightQuantArgs& a, hipStream_t stream);
+hipError_t launch_weight_dequant(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+size_t grouped_workspace_bytes(int64_t E);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace dsfp8

@@ -1,0 +1,342 @@
+// Bandwidth-bound kernels of the FP8 linear layer on gfx950:
+//   act_quant (optionally fused with SiLU(g)*u), weight block quantisation,
+//   weight dequantisation.
+//
+// act_quant ("DeepSeek-V3 Administrator & Developer Guide", 8.5.1): one
+// 128-element block of a row is handled by one DPP row of 16 lanes, 8 elements
+// (16 bytes of bf16) per lane, so a wavefront covers four blocks with one
+// 16-byte load per lane and the block maximum is a four-step DPP reduction
+// that never leaves the row.  Each lane computes the block scale and its
+// correctly rounded reciprocal once, and every quotient x/s costs one multiply
+// and two fma.  Work is distributed as (row, block) units in a grid-stride
+// loop sized to the machine; each lane keeps UNITS independent 16-byte loads
+// in flight.
+#include "device.h"
+#include "launch.h"
+
+namespace dsfp8 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 mk4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v;
+  v.x = a; v.y = b; v.z = c; v.w = d;
+  return v;
+}
+
+struct Unit {
+  int64_t m;
+  int64_t b;
+};
+
+// Activation quantisation of one (row, block) unit held by 16 lanes.
+// `v` holds this lane's 8 values (already SiLU-gated if fused); `valid` says
+// which of them are real columns.  Writes y, s (and nothing for padding).
+template <bool VEC>
+__device__ __forceinline__ void quantise_unit(const float (&v)[8], int nvalid, const ActQuantArgs& a,
+                                              int64_t m, int64_t b, int lane16, bool live) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, j < nvalid ? fabsf(v[j]) : 0.0f);
+  amax = max_row16(amax);
+  const float s = block_scale(amax, a.ue8m0);
+  const float r = 1.0f / s;
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = div_by_scale(v[j], s, r);
+  if (!live) return;
+  const int64_t col = b * kBlock + lane16 * 8;
+  uint8_t* yrow = a.y + m * a.ldy;
+  if (VEC) {
+    if (nvalid == 8) {
+      u32x2 o;
+      o.x = pack_e4m3x4(q[0], q[1], q[2], q[3]);
+      o.y = pack_e4m3x4(q[4], q[5], q[6], q[7]);
+      *reinterpret_cast<u32x2*>(yrow + col) = o;
+    }
+  } else {
+    uint32_t lo = pack_e4m3x4(q[0], q[1], q[2], q[3]);
+    uint32_t hi = pack_e4m3x4(q[4], q[5], q[6], q[7]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < nvalid) yrow[col + j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xff);
+  }
+  if (lane16 == 0) a.s[m * a.lds + b] = s;
+}
+
+// Load this lane's 8 bf16 values of one unit.  VEC: one 16-byte load (the
+// host guarantees alignment and K % 8 == 0, so a lane's 8 columns are either
+// all real or all padding).
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t m, int64_t col, int64_t K,
+                                       bool live) {
+  u32x4 w = mk4(0, 0, 0, 0);
+  if (!live) return w;
+  const uint16_t* p = base + m * ld + col;
+  if (VEC) {
+    if (col < K) w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  } else {
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (col + j < K) ? (uint32_t)p[j] : 0u;
+    w.x = e[0] | (e[1] << 16);
+    w.y = e[2] | (e[3] << 16);
+    w.z = e[4] | (e[5] << 16);
+    w.w = e[6] | (e[7] << 16);
+  }
+  return w;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 w, float (&v)[8]) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// SiLU(g) * u in fp32 with the hardware exponential, rounded to bf16 and
+// widened back, so that the quantiser sees exactly the bf16 value h.
+__device__ __forceinline__ float silu_mul_bf16(float g, float u, __bf16* hb) {
+  const float e = __expf(-g);
+  const float h = (g / (1.0f + e)) * u;
+  *hb = (__bf16)h;
+  return (float)(*hb);
+}
+
+template <bool VEC, bool FUSED>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int64_t nb, int64_t step_m,
+                                                             int64_t step_b) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t group = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;
+  Unit u;
+  u.m = group / nb;
+  u.b = group - u.m * nb;
+  while (u.m < a.M) {
+    Unit us[kUnroll];
+    u32x4 wg[kUnroll], wu[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      us[i] = u;
+      const bool live = u.m < a.M;
+      const int64_t col = u.b * kBlock + lane16 * 8;
+      wg[i] = load8<VEC>(a.g, a.ldg, u.m, col, a.K, live);
+      if (FUSED) wu[i] = load8<VEC>(a.u, a.ldu, u.m, col, a.K, live);
+      u.b += step_b;
+      u.m += step_m;
+      if (u.b >= nb) {
+        u.b -= nb;
+        u.m += 1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const bool live = us[i].m < a.M;
+      const int64_t col = us[i].b * kBlock + lane16 * 8;
+      int64_t rem = a.K - col;
+      const int nvalid = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+      float v[8];
+      unpack8(wg[i], v);
+      if (FUSED) {
+        float uv[8];
+        unpack8(wu[i], uv);
+        __bf16 hb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = silu_mul_bf16(v[j], uv[j], &hb[j]);
+        if (a.h != nullptr && live) {
+          uint16_t* hrow = a.h + us[i].m * a.ldh + col;
+          if (VEC) {
+            if (nvalid == 8) {
+              u32x4 o;
+              o.x = pack_bf16x2(v[0], v[1]);
+              o.y = pack_bf16x2(v[2], v[3]);
+              o.z = pack_bf16x2(v[4], v[5]);
+              o.w = pack_bf16x2(v[6], v[7]);
+              *reinterpret_cast<u32x4*>(hrow) = o;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < nvalid) hrow[j] = __builtin_bit_cast(uint16_t, hb[j]);
+          }
+        }
+      }
+      quantise_unit<VEC>(v, nvalid, a, us[i].m, us[i].b, lane16, live);
+    }
+  }
+}
+
+// ---- weight block quantisation ---------------------------------------------------
+//
+// One workgroup per 128x128 block: 16 lanes cover a 128-column row segment
+// (8 columns each), 16 row segments per pass, 8 passes.  The block's values
+// stay in registers between the maximum and the quantisation, so the weight
+// is read from memory once.
+
+template <typename T>
+__device__ __forceinline__ float load_w(const T* p);
+template <>
+__device__ __forceinline__ float load_w<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_w<uint16_t>(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void weight_quant_kernel(WeightQuantArgs a) {
+  __shared__ float wave_max[kThreads / 64];
+  const int t = threadIdx.x;
+  const int lane16 = t & 15;
+  const int seg = t >> 4;                 // 0..15
+  const int64_t bj = blockIdx.x, bi = blockIdx.y;
+  const int64_t c0 = bj * kBlock + lane16 * 8;
+  const T* w = reinterpret_cast<const T*>(a.w);
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int64_t n = bi * kBlock + p * 16 + seg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = n < a.N && c0 + j < a.K;
+      v[p][j] = ok ? load_w<T>(w + n * a.ldw + c0 + j) : 0.0f;
+      amax = fmaxf(amax, fabsf(v[p][j]));
+    }
+  }
+  amax = max_wave(amax);
+  if ((t & 63) == 0) wave_max[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float s = block_scale(amax, a.ue8m0);
+  const float r = 1.0f / s;
+  if (t == 0) a.S[bi * a.ldS + bj] = s;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int64_t n = bi * kBlock + p * 16 + seg;
+    if (n >= a.N) continue;
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = div_by_scale(v[p][j], s, r);
+    const uint32_t lo = pack_e4m3x4(q[0], q[1], q[2], q[3]);
+    const uint32_t hi = pack_e4m3x4(q[4], q[5], q[6], q[7]);
+    uint8_t* out = a.q + n * a.ldq + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.K) out[j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xff);
+  }
+}
+
+// ---- weight dequantisation -----------------------------------------------------
+//
+// ("DeepSeek-V3 Administrator & Developer Guide", 8.5.2.)  Each lane converts
+// 16 consecutive e4m3 bytes of one row with eight v_cvt_pk_f32_fp8, multiplies
+// each value by the block's scale in fp32, rounds pairs to bf16 with eight
+// v_cvt_pk_bf16_f32 and stores 32 bytes.  A workgroup covers 4096 columns of
+// kDqRows rows.
+
+constexpr int kDqRows = 4;
+
+__device__ __forceinline__ void dequant16(const u32x4 w, float s, u32x4& o0, u32x4& o1) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], false);
+    f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], true);
+    out[2 * i] = pack_bf16x2(lo[0] * s, lo[1] * s);
+    out[2 * i + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+  }
+  o0 = mk4(out[0], out[1], out[2], out[3]);
+  o1 = mk4(out[4], out[5], out[6], out[7]);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void weight_dequant_kernel(DequantArgs a) {
+  const int64_t col = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 16;
+  if (col >= a.K) return;
+  const int64_t row0 = (int64_t)blockIdx.y * kDqRows;
+  const int64_t kb = col / kBlock;
+#pragma unroll
+  for (int r = 0; r < kDqRows; ++r) {
+    const int64_t n = row0 + r;
+    if (n >= a.N) return;
+    const float s = a.S[(n / kBlock) * a.ldS + kb];
+    const uint8_t* src = a.w + n * a.ldw + col;
+    uint16_t* dst = a.out + n * a.ldo + col;
+    if (VEC) {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      u32x4 o0, o1;
+      dequant16(w, s, o0, o1);
+      __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(dst) + 1);
+    } else {
+      uint32_t bytes[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bytes[j] = (col + j < a.K) ? src[j] : 0u;
+      u32x4 w = mk4(bytes[0] | bytes[1] << 8 | bytes[2] << 16 | bytes[3] << 24,
+                           bytes[4] | bytes[5] << 8 | bytes[6] << 16 | bytes[7] << 24,
+                           bytes[8] | bytes[9] << 8 | bytes[10] << 16 | bytes[11] << 24,
+                           bytes[12] | bytes[13] << 8 | bytes[14] << 16 | bytes[15] << 24);
+      u32x4 o0, o1;
+      dequant16(w, s, o0, o1);
+      const uint32_t outw[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (col + j < a.K) dst[j] = (uint16_t)((outw[j >> 1] >> (16 * (j & 1))) & 0xffff);
+    }
+  }
+}
+
+inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
+  if (a.M == 0 || a.K == 0) return hipSuccess;
+  const int64_t nb = (a.K + kBlock - 1) / kBlock;
+  const int64_t units = a.M * nb;
+  const bool fused = a.u != nullptr;
+  // 16-byte loads of x (and u), 8-byte stores of y, 16-byte stores of h.
+  bool vec = (a.K % 8 == 0) && aligned(a.g, 16) && (a.ldg % 8 == 0) && aligned(a.y, 8) && (a.ldy % 8 == 0);
+  if (fused) vec = vec && aligned(a.u, 16) && (a.ldu % 8 == 0);
+  if (a.h) vec = vec && aligned(a.h, 16) && (a.ldh % 8 == 0);
+  const int64_t groups_per_wg = kThreads / 16;
+  const int64_t want = (units + groups_per_wg * kUnroll - 1) / (groups_per_wg * kUnroll);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t grid = want < cap ? want : cap;
+  const int64_t G = grid * groups_per_wg;
+  const int64_t step_m = G / nb, step_b = G % nb;
+  dim3 g((unsigned)grid), blk(kThreads);
+  if (fused) {
+    if (vec) hipLaunchKernelGGL((act_quant_kernel<true, true>), g, blk, 0, stream, a, nb, step_m, step_b);
+    else hipLaunchKernelGGL((act_quant_kernel<false, true>), g, blk, 0, stream, a, nb, step_m, step_b);
+  } else {
+    if (vec) hipLaunchKernelGGL((act_quant_kernel<true, false>), g, blk, 0, stream, a, nb, step_m, step_b);
+    else hipLaunchKernelGGL((act_quant_kernel<false, false>), g, blk, 0, stream, a, nb, step_m, step_b);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_quant(const WeightQuantArgs& a, hipStream_t stream) {
+  if (a.N == 0 || a.K == 0) return hipSuccess;
+  dim3 g((unsigned)((a.K + kBlock - 1) / kBlock), (unsigned)((a.N + kBlock - 1) / kBlock)), blk(kThreads);
+  if (a.bf16_in) hipLaunchKernelGGL((weight_quant_kernel<uint16_t>), g, blk, 0, stream, a);
+  else hipLaunchKernelGGL((weight_quant_kernel<float>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_dequant(const DequantArgs& a, hipStream_t stream) {
+  if (a.N == 0 || a.K == 0) return hipSuccess;
+  const bool vec = (a.K % 16 == 0) && aligned(a.w, 16) && (a.ldw % 16 == 0) && aligned(a.out, 16) &&
+                   (a.ldo % 8 == 0);
+  dim3 g((unsigned)((a.K + kThreads * 16 - 1) / (kThreads * 16)), (unsigned)((a.N + kDqRows - 1) / kDqRows));
+  dim3 blk(kThreads);
+  if (vec) hipLaunchKernelGGL((weight_dequant_kernel<true>), g, blk, 0, stream, a);
+  else hipLaunchKernelGGL((weight_dequant_kernel<false>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsfp8

@@ -1,0 +1,225 @@
+/*
+ * dsfp8 -- block-scaled FP8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libdsfp8.so.  Every entry point takes plain device pointers and
+ * sizes, enqueues its kernels on the caller's HIP stream and returns without
+ * synchronising.  The library allocates no memory and keeps no mutable global
+ * state; all buffers are owned by the caller.
+ *
+ * Sources of the operations (the DeepSeek-V3 inference code as described by):
+ *   [AG]  "DeepSeek-V3 Administrator & Developer Guide" (doccompiler.ai)
+ *   [UG]  "DeepSeek-V3 User Guide" (doccompiler.ai)
+ *   [DF]  "CodeVetter Repo Unpack: deepseek-v3 / Data flow"
+ *   [DS]  DocSearch (Algolia) index of the deepseek-ai/DeepSeek-V3 README
+ *
+ * Number formats
+ *   e4m3  OCP FP8 E4M3 "fn" (bias 7, max +-448, no infinity, NaN = S.1111.111),
+ *         i.e. torch.float8_e4m3fn ([DS] item 10).  Stored as one byte.
+ *   bf16  bfloat16, stored as two bytes.
+ *   Scales are IEEE fp32.
+ *
+ * Layout conventions (all entry points)
+ *   Matrices are row-major with the innermost dimension contiguous; "ld" is the
+ *   row stride in ELEMENTS and must be >= the row length.  Block size is fixed
+ *   at 128 ([DS] item 10: weight_block_size [128, 128]).  KB(K) = ceil(K/128).
+ *   Activation scales: fp32 [M, KB(K)], row stride lds (elements).
+ *   Weight scales:     fp32 [KB(N), KB(K)], row stride in elements.
+ *   A last block narrower than 128 (K or N not a multiple of 128) is treated
+ *   as zero-padded to 128 ([DS] item 3); only its real elements are read or
+ *   written.
+ *
+ * Error behaviour
+ *   Arguments are checked on the host before anything is enqueued.  A call
+ *   that returns a negative status has launched nothing and written nothing.
+ *   Sizes of zero are valid and launch nothing, except where an output must
+ *   still be written (a product with K == 0 writes zeros).  Device-resident
+ *   data (values, expert offsets) is not validated.  DSFP8_ERR_LAUNCH reports
+ *   a failure returned by the HIP runtime at launch.  No C++ exception
+ *   crosses this interface.
+ *
+ * Rounding
+ *   Scales and quotients are correctly rounded fp32 divisions; fp32 -> e4m3
+ *   is round-to-nearest-even with saturation to +-448, keeping the sign of
+ *   zero and producing subnormals; fp32 -> bf16 is round-to-nearest-even.
+ */
+#ifndef DSFP8_H
+#define DSFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSFP8_ABI_VERSION 1
+#define DSFP8_BLOCK 128
+
+typedef int dsfp8_status;
+
+enum {
+  DSFP8_OK = 0,
+  DSFP8_ERR_NULL = -1,       /* a required pointer is NULL                        */
+  DSFP8_ERR_SHAPE = -2,      /* a size is negative or exceeds the supported range */
+  DSFP8_ERR_LD = -3,         /* a leading dimension is smaller than its row       */
+  DSFP8_ERR_ALIGN = -4,      /* a pointer is not aligned to its element size      */
+  DSFP8_ERR_SCALE_FMT = -5,  /* unknown scale format                              */
+  DSFP8_ERR_WORKSPACE = -6,  /* workspace smaller than the size query returned    */
+  DSFP8_ERR_LAUNCH = -7,     /* the HIP runtime reported a launch failure         */
+  DSFP8_ERR_DTYPE = -8       /* unknown input element type                        */
+};
+
+/* Scale formats.  UE8M0 rounds each scale value up to a power of two
+ * ([UG] FAQ "What is scale_fmt: ue8m0?"; [AG] 8.5.1); the scale is still
+ * stored as fp32. */
+enum { DSFP8_SCALE_FP32 = 0, DSFP8_SCALE_UE8M0 = 1 };
+
+/* Element types accepted by dsfp8_weight_quant. */
+enum { DSFP8_DTYPE_F32 = 0, DSFP8_DTYPE_BF16 = 1 };
+
+/* Library ABI version (DSFP8_ABI_VERSION of the build). */
+int dsfp8_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* dsfp8_status_string(dsfp8_status status);
+
+/*
+ * Activation quantisation, [AG] 8.5.1 act_quant_kernel; [DF] (FP8 bullet)
+ * states that the per-block scales are kept as an fp32 tensor.
+ *
+ * For every row m and 128-column block b of x:
+ *   amax   = max |x[m, k]| over the block's real columns (fp32)
+ *   s      = max(amax, 1e-4f) / 448             (fp32 division)
+ *   s      = 2^ceil(log2 s)                     if scale_fmt == UE8M0 (exact)
+ *   y[m,k] = e4m3(x[m,k] / s)                   (fp32 division, RNE, saturating)
+ *   s_out[m, b] = s
+ *
+ *   x      bf16 [M, K], row stride ldx >= K            (device, read)
+ *   y      e4m3 [M, K], row stride ldy >= K            (device, written)
+ *   s      fp32 [M, KB(K)], row stride lds >= KB(K)    (device, written)
+ * K need not be a multiple of 128 (the pages' assertion that it is is relaxed;
+ * the partial block follows the zero-padding rule).
+ * Errors: NULL (x/y/s NULL with M*K > 0), SHAPE (M or K < 0), LD, ALIGN (x not
+ * 2-byte or s not 4-byte aligned), SCALE_FMT, LAUNCH.
+ */
+dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx,
+                             void* y, int64_t ldy, float* s, int64_t lds,
+                             int scale_fmt, hipStream_t stream);
+
+/*
+ * Fused SiLU-gate and activation quantisation for the feed-forward step
+ * between the up- and down-projections, [AG] 1.2 (MLP / Expert: w2(SiLU(w1 x)
+ * * w3 x)) followed by [AG] 8.5.1.
+ *
+ *   h[m,i] = bf16( SiLU(g[m,i]) * u[m,i] )       SiLU(v) = v / (1 + e^-v), fp32
+ *   (y, s) = act_quant(h)                        exactly as dsfp8_act_quant
+ *
+ *   g, u   bf16 [M, I], row strides ldg, ldu >= I  (device, read; g and u may be
+ *          the two halves of one [M, 2I] product, e.g. u = g + I, ldg = ldu = 2I)
+ *   y      e4m3 [M, I], row stride ldy             (device, written)
+ *   s      fp32 [M, KB(I)], row stride lds         (device, written)
+ *   h      bf16 [M, I], row stride ldh, or NULL    (device, written if not NULL)
+ * The exponential is the hardware's, so h is reproducible only to within one
+ * bf16 unit in the last place of a correctly rounded evaluation; (y, s) are
+ * always act_quant of the h that this call computes.
+ * Errors: as dsfp8_act_quant.
+ */
+dsfp8_status dsfp8_silu_mul_act_quant(const void* g, int64_t ldg,
+                                      const void* u, int64_t ldu,
+                                      int64_t M, int64_t I,
+                                      void* y, int64_t ldy, float* s, int64_t lds,
+                                      void* h, int64_t ldh,
+                                      int scale_fmt, hipStream_t stream);
+
+/*
+ * Weight block quantisation: produces the stored weight format of [DS] item 3
+ * (weight_scale_inv holds one fp32 multiplier per 128x128 block, a block is
+ * dequantised by multiplying it by that value, and a block that is not
+ * 128-aligned is zero-padded when its scale is computed) from real-valued
+ * weights.  The scale of a block mirrors act_quant:
+ *   S[i, j] = max(max |w| over the block, 1e-4f) / 448   (optionally UE8M0)
+ *   q[n, k] = e4m3(w[n, k] / S[n/128, k/128])
+ *
+ *   w      fp32 or bf16 (dtype) [N, K], row stride ldw  (device, read)
+ *   q      e4m3 [N, K], row stride ldq                  (device, written)
+ *   S      fp32 [KB(N), KB(K)], row stride ldS          (device, written)
+ * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, DTYPE, LAUNCH.
+ */
+dsfp8_status dsfp8_weight_quant(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw,
+                                void* q, int64_t ldq, float* S, int64_t ldS,
+                                int scale_fmt, hipStream_t stream);
+
+/*
+ * Weight dequantisation, [AG] 8.5.2 weight_dequant_kernel and [DS] item 3:
+ *   out[n, k] = bf16( fp32( dec(w[n, k]) * S[n/128, k/128] ) )
+ * (the product is rounded to fp32, then to bf16, as the pages load as fp32,
+ * multiply, and store in the default dtype).
+ *
+ *   w      e4m3 [N, K], row stride ldw                 (device, read)
+ *   S      fp32 [KB(N), KB(K)], row stride ldS         (device, read)
+ *   out    bf16 [N, K], row stride ldo                 (device, written)
+ * Errors: NULL, SHAPE, LD, ALIGN, LAUNCH.
+ */
+dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t ldw,
+                                  const float* S, int64_t ldS,
+                                  void* out, int64_t ldo, hipStream_t stream);
+
+/*
+ * Block-scaled FP8 product, [AG] 8.5.3 fp8_gemm_kernel and 6.3 (linear():
+ * y = x W^T with W [out, in]):
+ *   C[m, n] = bf16( sum_b  a_s[m, b] * b_s[n/128, b] * sum_{k in block b} dec(A[m,k]) dec(B[n,k]) )
+ * accumulated in fp32; the order of accumulation is unspecified.
+ *
+ *   A      e4m3 [M, K], row stride lda                  (device, read)
+ *   a_s    fp32 [M, KB(K)], row stride ldas             (device, read)
+ *   B      e4m3 [N, K], row stride ldb (the weight)     (device, read)
+ *   b_s    fp32 [KB(N), KB(K)], row stride ldbs         (device, read)
+ *   C      bf16 [M, N], row stride ldc                  (device, written)
+ *   workspace / workspace_bytes: scratch of at least
+ *          dsfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
+ * Errors: NULL, SHAPE, LD, ALIGN, WORKSPACE, LAUNCH.
+ */
+dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas,
+                        const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
+                        void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Grouped block-scaled FP8 product over per-expert row ranges: the batched form
+ * of the routed-expert loop of [AG] 6.4 / 8.4 (each expert's tokens pass
+ * through that expert's FP8 linear layer).  Rows of A are sorted by expert;
+ * expert e owns rows [offsets[e], offsets[e+1]) and has its own weight
+ * B[e] [N, K] and scale grid b_s[e] [KB(N), KB(K)]:
+ *   C[o_e:o_{e+1}] = dsfp8_gemm(A[o_e:o_{e+1}], a_s[o_e:o_{e+1}], B[e], b_s[e])
+ *
+ *   A        e4m3 [M_total, K], row stride lda              (device, read)
+ *   a_s      fp32 [M_total, KB(K)], row stride ldas         (device, read)
+ *   B        e4m3 [E, N, K]: row stride ldb, expert stride N*ldb       (device)
+ *   b_s      fp32 [E, KB(N), KB(K)]: row stride ldbs, expert stride
+ *            KB(N)*ldbs                                     (device, read)
+ *   offsets  int32 [E+1] in DEVICE memory, offsets[0] = 0, non-decreasing,
+ *            offsets[E] = M_total.  Not validated (that would need a host
+ *            synchronisation); the kernels clamp every range to [0, M_total],
+ *            so malformed offsets give unspecified output but no access
+ *            outside A, a_s or C.  Experts with no rows cost nothing.
+ *   C        bf16 [M_total, N], row stride ldc              (device, written)
+ * The combine step (scatter-add of each row times its routing weight) is not
+ * part of this call.
+ * Errors: NULL, SHAPE (E < 1, or E > 65536), LD, ALIGN, WORKSPACE, LAUNCH.
+ */
+dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas,
+                                const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
+                                const int32_t* offsets, int64_t E, int64_t M_total,
+                                int64_t N, int64_t K, void* C, int64_t ldc,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSFP8_H */

@@ -1,0 +1,144 @@
+"""The C ABI on the host (no GPU, no kernel launch).
+
+libdsfp8.so must load without a GPU and export every function that
+include/dsfp8.h declares.  Argument validation runs before any HIP call, so
+each error status can be provoked here with fake (never dereferenced)
+pointers; only calls that are rejected are made.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp8_act_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsfp8.h")
+
+OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+P = 0x10000          # a fake, 256-byte aligned device address (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dsfp8_status|size_t|int|const char\*)\s+(dsfp8_\w+)\(", text, re.M)))
+
+
+def header_constant(name):
+    m = re.search(rf"{name}\s*=?\s*(-?\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_scaled_fp8_act_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.dsfp8_abi_version() == header_constant("#define DSFP8_ABI_VERSION")
+    for st in (OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE):
+        s = lib.dsfp8_status_string(st)
+        assert s and s != b"unknown status"
+    assert lib.dsfp8_status_string(12345) == b"unknown status"
+
+
+def test_status_codes_match_header():
+    for name, v in [("DSFP8_ERR_NULL", NULL), ("DSFP8_ERR_SHAPE", SHAPE), ("DSFP8_ERR_LD", LD),
+                    ("DSFP8_ERR_ALIGN", ALIGN), ("DSFP8_ERR_SCALE_FMT", FMT), ("DSFP8_ERR_WORKSPACE", WS),
+                    ("DSFP8_ERR_LAUNCH", LAUNCH), ("DSFP8_ERR_DTYPE", DTYPE)]:
+        assert header_constant(name) == v
+
+
+def test_act_quant_validation(lib):
+    f = lib.dsfp8_act_quant
+    assert f(P, -1, 128, 128, P, 128, P, 1, 0, None) == SHAPE
+    assert f(P, 4, 1 << 31, 1 << 31, P, 1 << 31, P, 1 << 24, 0, None) == SHAPE
+    assert f(P, 4, 128, 128, P, 128, P, 1, 2, None) == FMT
+    assert f(None, 4, 128, 128, P, 128, P, 1, 0, None) == NULL
+    assert f(P, 4, 128, 128, None, 128, P, 1, 0, None) == NULL
+    assert f(P, 4, 128, 128, P, 128, None, 1, 0, None) == NULL
+    assert f(P, 4, 128, 100, P, 128, P, 1, 0, None) == LD
+    assert f(P, 4, 128, 128, P, 127, P, 1, 0, None) == LD
+    assert f(P, 4, 200, 200, P, 200, P, 1, 0, None) == LD          # scales need ceil(200/128) = 2
+    assert f(P + 1, 4, 128, 128, P, 128, P, 1, 0, None) == ALIGN    # bf16 needs 2-byte alignment
+    assert f(P, 4, 128, 128, P, 128, P + 2, 1, 0, None) == ALIGN    # fp32 needs 4
+    # empty problems are valid and launch nothing
+    assert f(None, 0, 128, 128, None, 128, None, 1, 0, None) == OK
+    assert f(None, 5, 0, 0, None, 0, None, 0, 0, None) == OK
+
+
+def test_silu_and_weight_validation(lib):
+    f = lib.dsfp8_silu_mul_act_quant
+    assert f(P, 256, P, 256, 4, 256, P, 256, P, 2, None, 0, 9, None) == FMT
+    assert f(P, 256, None, 256, 4, 256, P, 256, P, 2, None, 0, 0, None) == NULL
+    assert f(P, 256, P, 256, 4, 256, P, 256, P, 2, P, 100, 0, None) == LD
+    assert f(None, 256, None, 256, 0, 256, None, 256, None, 2, None, 0, 0, None) == OK
+    q = lib.dsfp8_weight_quant
+    assert q(P, 7, 128, 128, 128, P, 128, P, 1, 0, None) == DTYPE
+    assert q(P, 0, 128, 128, 128, P, 128, P, 1, 3, None) == FMT
+    assert q(P + 2, 0, 128, 128, 128, P, 128, P, 1, 0, None) == ALIGN  # fp32 input
+    assert q(P, 0, 300, 128, 128, P, 128, P, 0, 0, None) == LD         # scale grid is [3, 1]
+    d = lib.dsfp8_weight_dequant
+    assert d(P, -5, 128, 128, P, 1, P, 128, None) == SHAPE
+    assert d(None, 5, 128, 128, P, 1, P, 128, None) == NULL
+    assert d(P, 5, 128, 128, P, 1, P + 1, 128, None) == ALIGN
+    assert d(P, 5, 128, 64, P, 1, P, 128, None) == LD
+
+
+def test_gemm_validation(lib):
+    g = lib.dsfp8_gemm
+    # A, lda, a_s, ldas, B, ldb, b_s, ldbs, C, ldc, M, N, K, ws, wsb, stream
+    assert g(P, 256, P, 2, P, 256, P, 2, P, 64, -8, 64, 256, None, 0, None) == SHAPE
+    assert g(None, 256, P, 2, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == NULL
+    assert g(P, 255, P, 2, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
+    assert g(P, 256, P, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
+    assert g(P, 256, P, 2, P, 256, P, 2, P, 63, 8, 64, 256, None, 0, None) == LD
+    assert g(P, 256, P + 1, 2, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == ALIGN
+    assert g(P, 256, P, 2, P, 256, P, 2, P + 1, 64, 8, 64, 256, None, 0, None) == ALIGN
+    assert lib.dsfp8_gemm_workspace_bytes(4096, 18432, 7168) == 0
+
+
+def test_grouped_validation(lib):
+    g = lib.dsfp8_grouped_gemm
+    # A, lda, a_s, ldas, B, ldb, b_s, ldbs, offsets, E, M, N, K, C, ldc, ws, wsb, stream
+    args = [P, 256, P, 2, P, 256, P, 2, P, 4, 100, 64, 256, P, 64, P, 1 << 20, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["A", "lda", "a_s", "ldas", "B", "ldb", "b_s", "ldbs", "offsets", "E", "M", "N", "K", "C",
+                 "ldc", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return g(*a)
+
+    assert call(E=0) == SHAPE
+    assert call(E=70000) == SHAPE
+    assert call(offsets=None) == NULL
+    assert call(offsets=P + 2) == ALIGN
+    assert call(ldb=100) == LD
+    assert call(ldbs=1) == LD
+    need = lib.dsfp8_grouped_gemm_workspace_bytes(4, 100, 64, 256)
+    assert need >= 5 * 4
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == NULL
+    assert lib.dsfp8_grouped_gemm_workspace_bytes(0, 1, 1, 1) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
+        _lib.load()

@@ -1,0 +1,200 @@
+"""GPU parity of act_quant and the fused SiLU-gate quantiser against the oracle.
+
+Bit-exact: e4m3 bytes of y and the fp32 bits of s (Admin Guide 8.5.1, ue8m0
+per the User Guide FAQ).  Shapes: every workload's activation shape (the
+largest ones on sampled rows, whose quantisation is row-independent), ragged
+K, strided rows, the unaligned (scalar) path, and the degenerate cases:
+empty, zero blocks, signed zeros, clamp boundary, overflow of x/s past 448,
+tiny and huge magnitudes, and an exhaustive sweep of (scale significand,
+element significand) pairs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_act_amd as ds
+from block_scaled_fp8_act_amd import inputs as I
+from oracle import formats as F
+from oracle import glue
+from oracle import quant as Q
+
+from gpu_helpers import dev_bf16, host_bits16, host_f32_bits, host_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_compare(x_bits, fmt="fp32", x_dev=None):
+    xd = dev_bf16(x_bits) if x_dev is None else x_dev
+    y, s = ds.act_quant(xd, fmt)
+    torch.cuda.synchronize()
+    yr, sr = Q.act_quant(x_bits, ue8m0=(fmt == "ue8m0"))
+    yg, sg = host_u8(y), host_f32_bits(s)
+    bad_y = np.argwhere(yg != yr)
+    assert bad_y.size == 0, f"{len(bad_y)} y mismatches, first {bad_y[:3].tolist()}"
+    assert np.array_equal(sg, sr.view(np.uint32)), "scale mismatch"
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_tiny(fmt):
+    run_and_compare(I.activations((16, 512), I.TINY, 0), fmt)
+
+
+def test_decode_with_outliers():
+    w = I.WORKLOADS["decode_qa"].dims
+    run_and_compare(I.activations((32, 7168), I.DECODE_QA, 0, outlier_frac=w["outlier_frac"],
+                                  outlier_scale=w["outlier_scale"]))
+
+
+@pytest.mark.parametrize("fmt", ["ue8m0", "fp32"])
+def test_ragged_k1000(fmt):
+    run_and_compare(I.activations((333, 1000), I.RAGGED, 0), fmt)
+
+
+def test_dense_ffn_input_full():
+    run_and_compare(I.activations((4096, 7168), I.DENSE_FFN, 0))
+
+
+def test_large_shapes_sampled_rows():
+    # [4096, 18432] (down-projection input) and [32768, 7168] (routed rows):
+    # quantise on the GPU, compare 300 sampled rows with the oracle.
+    for shape, cid in (((4096, 18432), I.DENSE_FFN), ((32768, 7168), I.MOE)):
+        x = I.activations(shape, cid, 7)
+        y, s = ds.act_quant(dev_bf16(x))
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(1).choice(shape[0], 300, replace=False))
+        rows[-1] = shape[0] - 1
+        yr, sr = Q.act_quant(x[rows])
+        assert np.array_equal(host_u8(y[torch.from_numpy(rows).cuda()]), yr)
+        assert np.array_equal(host_f32_bits(s[torch.from_numpy(rows).cuda()]), sr.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (5, 129), (2, 130), (7, 1001), (1, 128), (64, 8)])
+def test_odd_shapes(M, K):
+    g = np.random.default_rng(M * 1000 + K)
+    x = F.f32_to_bf16((g.standard_normal((M, K)) * 3).astype(np.float32))
+    run_and_compare(x)
+    run_and_compare(x, "ue8m0")
+
+
+def test_strided_rows():
+    g = np.random.default_rng(3)
+    big = F.f32_to_bf16(g.standard_normal((40, 1024)).astype(np.float32))
+    xd = dev_bf16(big)[:, :640]            # ld = 1024 > K = 640
+    run_and_compare(big[:, :640].copy(), x_dev=xd)
+    xd2 = dev_bf16(big)[:, 3:643]          # unaligned start: scalar path
+    run_and_compare(big[:, 3:643].copy(), x_dev=xd2)
+
+
+def test_empty():
+    y, s = ds.act_quant(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
+    assert y.shape == (0, 256) and s.shape == (0, 2)
+    y, s = ds.act_quant(torch.empty((4, 0), dtype=torch.bfloat16, device="cuda"))
+    assert y.shape == (4, 0) and s.shape == (4, 0)
+
+
+def test_degenerate_values():
+    rows = []
+    z = np.zeros(256, np.float32)
+    rows.append(z)                                        # all zero -> clamp
+    rows.append(-z)                                       # all -0
+    r = z.copy(); r[5] = 3e-5; r[6] = -1e-6; rows.append(r)           # amax below clamp
+    r = z.copy(); r[:] = 1e-4; rows.append(r)             # amax at the clamp
+    r = np.full(256, 1e-38, np.float32); rows.append(r)   # tiny magnitudes (subnormal quotients)
+    r = np.full(256, 3.0e38, np.float32); r[1::2] *= -1; rows.append(r)   # near bf16 max
+    g = np.random.default_rng(4)
+    r = g.standard_normal(256).astype(np.float32); r[0] = 1e30; rows.append(r)   # one huge value
+    r = g.standard_normal(256).astype(np.float32); r[100] = -0.0; rows.append(r)
+    x = F.f32_to_bf16(np.stack(rows))
+    run_and_compare(x)
+    run_and_compare(x, "ue8m0")
+
+
+def test_overflow_past_448_saturates():
+    # Find bf16 amax values with fl(amax / fl(amax/448)) > 448.
+    cand = F.bf16_to_f32(np.arange(0x3F80, 0x4000, dtype=np.uint16))   # [1, 2)
+    s = cand / np.float32(448)
+    over = cand[(cand / s) > np.float32(448)]
+    assert over.size > 0
+    x = np.zeros((over.size, 128), np.float32)
+    x[:, 0] = over
+    x[:, 1] = -over
+    x[:, 2:] = over[:, None] * 0.3
+    xb = F.f32_to_bf16(x)
+    run_and_compare(xb)
+    y, _ = Q.act_quant(xb)
+    assert np.all(y[:, 0] == 0x7E) and np.all(y[:, 1] == 0xFE)
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_exhaustive_significand_pairs(fmt):
+    # Block (a, d): element 0 = amax with significand a (in [1, 2)); elements
+    # j = 1..127 have significand j at 2^-d with alternating sign.  Covers every
+    # (scale significand, element significand) pair at 13 relative binades.
+    amax = F.bf16_to_f32(np.arange(0x3F80, 0x4000, dtype=np.uint16))
+    sig = F.bf16_to_f32(np.arange(0x3F80, 0x4000, dtype=np.uint16))
+    blocks = []
+    for d in range(13):
+        b = np.empty((128, 128), np.float32)
+        b[:, 0] = amax
+        vals = sig[1:] * np.float32(2.0 ** -d)
+        vals[1::2] *= -1
+        b[:, 1:] = vals[None, :]
+        blocks.append(b)
+    x = F.f32_to_bf16(np.concatenate(blocks, axis=0).reshape(13 * 128, 128))
+    run_and_compare(x, fmt)
+    # and with the blocks scaled by powers of two across the exponent range
+    xs = F.f32_to_bf16(F.bf16_to_f32(x) * np.float32(2.0 ** -40))
+    run_and_compare(xs, fmt)
+    xl = F.f32_to_bf16(F.bf16_to_f32(x) * np.float32(2.0 ** 60))
+    run_and_compare(xl, fmt)
+
+
+# ---- fused SiLU gate + quantisation ----------------------------------------------------
+
+def _silu_case(M, I_, seed):
+    g = I.activations((M, I_), I.DENSE_FFN, 100 + seed, std=1.7)
+    u = I.activations((M, I_), I.DENSE_FFN, 200 + seed, std=1.7)
+    return g, u
+
+
+@pytest.mark.parametrize("M,I_,fmt", [(64, 2048, "fp32"), (33, 1000, "ue8m0"), (5, 130, "fp32"),
+                                      (512, 18432, "fp32")])
+def test_silu_mul_act_quant(M, I_, fmt):
+    g, u = _silu_case(M, I_, M)
+    y, s, h = ds.silu_mul_act_quant(dev_bf16(g), dev_bf16(u), fmt, return_h=True)
+    torch.cuda.synchronize()
+    hg = host_bits16(h)
+    href = glue.silu_mul(g, u)
+    # h: within one bf16 ulp of the correctly rounded value, rarely different
+    hv, rv = F.bf16_to_f32(hg).astype(np.float64), F.bf16_to_f32(href).astype(np.float64)
+    diff = hg != href
+    ulp = np.abs(rv) * 2.0 ** -7 + 1e-40
+    assert np.all(np.abs(hv - rv) <= ulp), "SiLU gate off by more than one bf16 ulp"
+    assert diff.mean() < 1e-3, f"{diff.mean():.2e} of h differ from the correctly rounded value"
+    # (y, s) on blocks whose h agrees bit-exactly must equal the oracle's act_quant
+    yr, sr = Q.act_quant(href, ue8m0=(fmt == "ue8m0"))
+    nb = (I_ + 127) // 128
+    pad = np.zeros((M, nb * 128), bool)
+    pad[:, :I_] = diff
+    clean = ~pad.reshape(M, nb, 128).any(axis=2)
+    assert np.array_equal(host_f32_bits(s)[clean], sr.view(np.uint32)[clean])
+    yg = host_u8(y)
+    colblk = np.arange(I_) // 128
+    mask = clean[:, colblk]
+    assert np.array_equal(yg[mask], yr[mask])
+    # and (y, s) are exactly act_quant of the h this call produced (GPU vs GPU)
+    y2, s2 = ds.act_quant(h, fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
+
+
+def test_silu_mul_strided_halves():
+    # g and u as the two halves of one [M, 2I] product (row stride 2I).
+    M, I_ = 48, 1024
+    gu = I.activations((M, 2 * I_), I.DENSE_FFN, 300, std=1.7)
+    d = dev_bf16(gu)
+    y, s = ds.silu_mul_act_quant(d[:, :I_], d[:, I_:])
+    y2, s2 = ds.silu_mul_act_quant(dev_bf16(gu[:, :I_].copy()), dev_bf16(gu[:, I_:].copy()))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(s, s2)
