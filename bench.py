@@ -1,0 +1,404 @@
+"""Benchmark of the block-scaled FP8 linear layer on one MI355X.
+
+Headline workload: the dense FFN at prefill (4096 tokens, dim 7168, inter
+18432).  One step is the whole hot path of one FFN layer with every input
+already resident in HBM:
+
+    act_quant(x [4096, 7168])                          -> e4m3 + scales
+    gemm(x_q, [w1; w3] e4m3 [36864, 7168])             -> bf16 [4096, 36864]
+    silu_mul_act_quant(h1, h3)                         -> e4m3 [4096, 18432] + scales
+    gemm(h_q, w2 e4m3 [7168, 18432])                   -> bf16 [4096, 7168]
+
+``value`` is the step's GEMM work (3 x 2*4096*18432*7168 flop) divided by the
+step time, in TFLOP/s.  Every kernel launch is bracketed by HIP events on the
+launch stream, which gives each kernel's average duration; ``roofline``
+reports the dominant kernel (the up-projection GEMM) against the FP8 dense
+MFMA peak.  The other workloads (routed experts, weight dequantisation, the
+decode projection, the ragged ue8m0 case) are timed the same way and reported
+under ``other_workloads``.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_scaled_fp8_act_amd as ds  # noqa: E402
+from block_scaled_fp8_act_amd import inputs as I  # noqa: E402
+
+METRIC = "block-scaled FP8 GEMM TFLOP/s & % of MI355X FP8 MFMA peak; act_quant GB/s"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+
+
+def kb(n):
+    return (n + 127) // 128
+
+
+class Timer:
+    """Per-kernel HIP-event timing on the current (launch) stream."""
+
+    def __init__(self):
+        self.samples = {}
+        self.pending = []
+
+    def run(self, name, fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pending.append((name, e0, e1))
+
+    def collect(self):
+        torch.cuda.synchronize()
+        for name, e0, e1 in self.pending:
+            self.samples.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)  # us
+        self.pending = []
+
+    def avg_us(self, name):
+        return float(np.mean(self.samples[name]))
+
+    def reset(self):
+        self.samples = {}
+        self.pending = []
+
+
+# ---- dense FFN step ---------------------------------------------------------------------
+
+def setup_dense(dev):
+    d = I.WORKLOADS["dense_ffn"].dims
+    M, D, F = d["M"], d["dim"], d["inter"]
+    x = I.device_normal((M, D), seed=301, std=1.0, device=dev, dtype=torch.bfloat16)
+    w13 = I.device_normal((2 * F, D), seed=302, std=0.02, device=dev)
+    q13, s13 = ds.weight_quant(w13)
+    del w13
+    w2 = I.device_normal((D, F), seed=303, std=0.02, device=dev)
+    q2, s2 = ds.weight_quant(w2)
+    del w2
+    bufs = dict(
+        x=x, q13=q13, s13=s13, q2=q2, s2=s2,
+        xq=torch.empty((M, D), dtype=torch.uint8, device=dev),
+        xs=torch.empty((M, kb(D)), dtype=torch.float32, device=dev),
+        h13=torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev),
+        hq=torch.empty((M, F), dtype=torch.uint8, device=dev),
+        hs=torch.empty((M, kb(F)), dtype=torch.float32, device=dev),
+        out=torch.empty((M, D), dtype=torch.bfloat16, device=dev),
+    )
+    torch.cuda.synchronize()
+    return dict(M=M, D=D, F=F, b=bufs)
+
+
+def dense_step(st, T):
+    b, F = st["b"], st["F"]
+    T.run("act_quant", lambda: ds.act_quant(b["x"], out=(b["xq"], b["xs"])))
+    T.run("gemm_up", lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"]))
+    T.run("silu_mul_act_quant",
+          lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:], out=(b["hq"], b["hs"])))
+    T.run("gemm_down", lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"]))
+
+
+def gemm_bytes(M, N, K):
+    return M * K + N * K + 4 * (M * kb(K) + kb(N) * kb(K)) + 2 * M * N
+
+
+def aq_bytes(M, K, inputs=1):
+    return inputs * 2 * M * K + M * K + 4 * M * kb(K)
+
+
+# ---- other workloads ----------------------------------------------------------------------
+
+def bench_moe(dev, iters):
+    d = I.WORKLOADS["moe"].dims
+    E, D, F = d["experts"], d["dim"], d["inter"]
+    tok, off, counts = I.zipf_routing(d["tokens"], E, d["topk"], d["zipf_s"])
+    M = int(off[-1])
+    xt = I.device_normal((d["tokens"], D), seed=401, std=1.0, device=dev, dtype=torch.bfloat16)
+    x = xt[torch.from_numpy(tok).to(dev)].contiguous()
+    del xt
+    q13 = torch.empty((E, 2 * F, D), dtype=torch.uint8, device=dev)
+    s13 = torch.empty((E, kb(2 * F), kb(D)), dtype=torch.float32, device=dev)
+    q2 = torch.empty((E, D, F), dtype=torch.uint8, device=dev)
+    s2 = torch.empty((E, kb(D), kb(F)), dtype=torch.float32, device=dev)
+    for e in range(E):
+        w = I.device_normal((2 * F, D), seed=10_000 + e, std=0.02, device=dev)
+        q, s = ds.weight_quant(w)
+        q13[e].copy_(q)
+        s13[e].copy_(s)
+        w = I.device_normal((D, F), seed=20_000 + e, std=0.02, device=dev)
+        q, s = ds.weight_quant(w)
+        q2[e].copy_(q)
+        s2[e].copy_(s)
+    del w, q, s
+    offd = torch.from_numpy(off).to(dev)
+    xq = torch.empty((M, D), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, kb(D)), dtype=torch.float32, device=dev)
+    h13 = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
+    hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
+    hs = torch.empty((M, kb(F)), dtype=torch.float32, device=dev)
+    out = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ds._lib.load().dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
+    T = Timer()
+
+    def step():
+        T.run("act_quant", lambda: ds.act_quant(x, out=(xq, xs)))
+        T.run("grouped_up", lambda: ds.grouped_gemm(xq, xs, q13, s13, offd, out=h13, workspace=ws))
+        T.run("silu_mul_act_quant", lambda: ds.silu_mul_act_quant(h13[:, :F], h13[:, F:], out=(hq, hs)))
+        T.run("grouped_down", lambda: ds.grouped_gemm(hq, hs, q2, s2, offd, out=out, workspace=ws))
+
+    for _ in range(2):
+        step()
+    T.collect()
+    T.reset()
+    for _ in range(iters):
+        step()
+    T.collect()
+    flop_up, flop_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
+    by_up = M * D + E * 2 * F * D + 4 * (M * kb(D) + E * kb(2 * F) * kb(D)) + 2 * M * 2 * F
+    by_dn = M * F + E * D * F + 4 * (M * kb(F) + E * kb(D) * kb(F)) + 2 * M * D
+    res = {"workload": I.WORKLOADS["moe"].desc, "rows": M,
+           "expert_rows": {"min": int(counts.min()), "median": float(np.median(counts)),
+                           "max": int(counts.max())}}
+    for name, fl, by in (("grouped_up", flop_up, by_up), ("grouped_down", flop_dn, by_dn)):
+        us = T.avg_us(name)
+        roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
+        res[name] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
+                     "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3)}
+    for name, by in (("act_quant", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2))):
+        us = T.avg_us(name)
+        res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
+                     "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
+    step_us = sum(T.avg_us(n) for n in ("act_quant", "grouped_up", "silu_mul_act_quant", "grouped_down"))
+    res["step_us"] = round(step_us, 1)
+    del q13, q2
+    return res
+
+
+def bench_dequant(dev, iters):
+    N, K = 18432, 7168
+    w = I.device_normal((N, K), seed=501, std=0.02, device=dev)
+    res = {"workload": "weight_dequant e4m3 [18432, 7168] -> bf16"}
+    for fmt in ("fp32", "ue8m0"):
+        q, S = ds.weight_quant(w, fmt)
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        T = Timer()
+        for _ in range(3):
+            ds.weight_dequant(q, S, out=out)
+        torch.cuda.synchronize()
+        for _ in range(iters):
+            T.run("dq", lambda: ds.weight_dequant(q, S, out=out))
+        T.collect()
+        us = T.avg_us("dq")
+        by = N * K * 3 + 4 * kb(N) * kb(K)
+        res[fmt] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
+                    "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
+    return res
+
+
+def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
+    """act_quant + gemm on a small shape, rotating weight copies (> 512 MB in
+    total) so that neither the L2 nor the 256 MB Infinity Cache serves them."""
+    x = I.device_normal((M, K), seed=601, std=1.0, device=dev, dtype=torch.bfloat16)
+    if outlier:
+        cols = torch.from_numpy(np.random.default_rng(0).choice(K, int(round(0.01 * K)), replace=False)).to(dev)
+        x[:, cols] *= 20
+    copies = max(2, int(np.ceil(600e6 / (N * K))))
+    ws = []
+    for i in range(copies):
+        w = I.device_normal((N, K), seed=700 + i, std=0.02, device=dev)
+        ws.append(ds.weight_quant(w, fmt))
+    del w
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, kb(K)), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    T = Timer()
+    for i in range(copies + 3):
+        ds.act_quant(x, fmt, out=(xq, xs))
+        ds.gemm(xq, xs, *ws[i % copies], out=out)
+    torch.cuda.synchronize()
+    for i in range(iters):
+        T.run("act_quant", lambda: ds.act_quant(x, fmt, out=(xq, xs)))
+        q, s = ws[i % copies]
+        T.run("gemm", lambda: ds.gemm(xq, xs, q, s, out=out))
+    T.collect()
+    g_us, a_us = T.avg_us("gemm"), T.avg_us("act_quant")
+    fl, by = 2.0 * M * N * K, gemm_bytes(M, N, K)
+    roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
+    return {"workload": name, "gemm": {"us": round(g_us, 2), "tflops": round(fl / g_us / 1e6, 2),
+                                       "gbs": round(by / g_us / 1e3, 1), "roofline_us": round(roof_us, 2),
+                                       "frac_of_roofline": round(roof_us / g_us, 3)},
+            "act_quant": {"us": round(a_us, 2), "gbs": round(aq_bytes(M, K) / a_us / 1e3, 1)},
+            "weight_copies_rotated": copies}
+
+
+# ---- CPU baseline ---------------------------------------------------------------------------
+
+def cpu_baseline():
+    """The CPU oracle on a bounded sample of the dense FFN step.
+
+    Sample: 128 token rows; 1536 rows each of w1 and w3 (3072 outputs of the
+    up-projection) over the full K = 7168; SiLU gate; 1536 rows of w2 over
+    the first 1536 of its K columns.  Weights are drawn and quantised on the
+    host before timing; the timed part is act_quant, the up product, the gate,
+    act_quant of h and the down product, all in the oracle.  Reported as the
+    sample's GEMM flop per second.
+    """
+    import threadpoolctl
+    from oracle import gemm as G
+    from oracle import glue
+    from oracle import quant as Q
+
+    Ms, D, Fs = 128, 7168, 1536
+    x = I.activations((Ms, D), I.DENSE_FFN, 900)
+    w13 = Q.weight_quant(I.weights_f32((2 * Fs, D), I.DENSE_FFN, 901))
+    w2 = Q.weight_quant(I.weights_f32((Fs, Fs), I.DENSE_FFN, 902))
+    from oracle.formats import f32_to_bf16
+    t0 = time.perf_counter()
+    a, a_s = Q.act_quant(x)
+    h13 = f32_to_bf16(G.gemm(a, a_s, *w13))
+    h = glue.silu_mul(h13[:, :Fs], h13[:, Fs:])
+    hq, hs = Q.act_quant(h)
+    _ = G.gemm(hq, hs, *w2)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * Ms * 2 * Fs * D + 2.0 * Ms * Fs * Fs
+    try:
+        blas = threadpoolctl.threadpool_info()
+        threads = max([b.get("num_threads", 1) for b in blas] + [1])
+    except Exception:
+        threads = 1
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "dense FFN step on 128 tokens x (3072 up-projection outputs, K=7168) + SiLU gate + "
+                      "(1536 down outputs, K=1536); fp64 products through NumPy BLAS, quantisers in NumPy"}
+
+
+# ---- traffic (from the committed rocprofv3 counter summary) -----------------------------------
+
+def gemm_source_digest():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device.h"):
+        with open(os.path.join(ROOT, "block_scaled_fp8_act_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the up-projection GEMM, from the counter summary
+    in profiles/, or None if it was taken on a different GEMM source."""
+    path = os.path.join(ROOT, "profiles", "gemm_dense_ffn_up_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != gemm_source_digest():
+        return None
+    return float(t.group(1))
+
+
+# ---- main --------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X).", file=sys.stderr)
+        sys.exit(2)
+    ds._lib.load()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    st = setup_dense(dev)
+    T = Timer()
+    for _ in range(args.warmup):
+        dense_step(st, T)
+    T.collect()
+    T.reset()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.steps):
+        dense_step(st, T)
+    s1.record()
+    T.collect()
+    torch.cuda.synchronize()
+    step_ms = s0.elapsed_time(s1) / args.steps
+
+    M, D, F = st["M"], st["D"], st["F"]
+    fl_up, fl_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
+    total_flop = fl_up + fl_dn
+    value = total_flop / (step_ms * 1e-3) / 1e12
+    k = {}
+    for name, fl, by in (("gemm_up", fl_up, gemm_bytes(M, 2 * F, D)), ("gemm_down", fl_dn, gemm_bytes(M, D, F))):
+        us = T.avg_us(name)
+        k[name] = {"shape": [M, 2 * F if name == "gemm_up" else D, D if name == "gemm_up" else F],
+                   "us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
+                   "frac_of_fp8_peak": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+    for name, by in (("act_quant", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2))):
+        us = T.avg_us(name)
+        k[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
+                   "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}
+    up_us = T.avg_us("gemm_up")
+    achieved = fl_up / up_us / 1e6
+    traffic = recorded_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantised to e4m3 with 128x128 scales)",
+        "config": {"workload": "dense FFN prefill: act_quant [4096,7168] -> gemm [w1;w3] 4096x36864x7168 -> "
+                               "silu_mul_act_quant [4096,18432] -> gemm w2 4096x7168x18432",
+                   "tokens": M, "dim": D, "inter": F, "block": 128},
+        "roofline": {"bound": "mfma", "kernel": "gemm_up 4096x36864x7168", "achieved": round(achieved, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(up_us, 1)},
+        "kernels": k,
+        "act_quant_gbs": k["act_quant"]["gbs"],
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.quick:
+        others = {}
+        others["routed_experts"] = bench_moe(dev, 10)
+        others["weight_dequant"] = bench_dequant(dev, 20)
+        others["decode_qa"] = bench_small_gemm(dev, 50, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True)
+        others["ragged_ue8m0"] = bench_small_gemm(dev, 50, "ragged ue8m0: 333x2500x1000", 333, 2500, 1000,
+                                                  "ue8m0", False)
+        line["other_workloads"] = others
+    if not args.quick and not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

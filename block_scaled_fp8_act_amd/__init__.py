@@ -72,33 +72,47 @@ def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def act_quant(x, scale_fmt="fp32"):
+def _out(out, shape, dtype, device, name):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _mat(_bytes(out), name, (dtype,), dim=len(shape))
+    if tuple(out.shape) != tuple(shape) or out.device != device:
+        raise Dsfp8Error(f"{name} must be {tuple(shape)} on {device}, got {tuple(out.shape)} on {out.device}")
+    return _bytes(out)
+
+
+def act_quant(x, scale_fmt="fp32", out=None):
     """Quantise bf16 ``x [M, K]`` per row and per 128 columns.
 
     Returns ``(y uint8 [M, K], s float32 [M, ceil(K/128)])`` with x ~= e4m3(y) * s.
+    ``out`` may supply preallocated ``(y, s)`` (row strides are honoured).
     """
     _mat(x, "x", (torch.bfloat16,))
     M, K = x.shape
-    y = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty((M, kblocks(K)), dtype=torch.float32, device=x.device)
-    st = _lib.load().dsfp8_act_quant(x.data_ptr(), M, K, _ld(x), y.data_ptr(), K, s.data_ptr(), kblocks(K),
+    yo, so = out if out is not None else (None, None)
+    y = _out(yo, (M, K), torch.uint8, x.device, "y")
+    s = _out(so, (M, kblocks(K)), torch.float32, x.device, "s")
+    st = _lib.load().dsfp8_act_quant(x.data_ptr(), M, K, _ld(x), y.data_ptr(), _ld(y), s.data_ptr(), _ld(s),
                                      _fmt(scale_fmt), _stream(x))
     _check("act_quant", st)
     return y, s
 
 
-def silu_mul_act_quant(g, u, scale_fmt="fp32", return_h=False):
-    """``act_quant(bf16(SiLU(g) * u))`` in one pass; optionally also return h."""
+def silu_mul_act_quant(g, u, scale_fmt="fp32", return_h=False, out=None):
+    """``act_quant(bf16(SiLU(g) * u))`` in one pass; optionally also return h.
+
+    ``out`` may supply preallocated ``(y, s)``."""
     _mat(g, "g", (torch.bfloat16,))
     _mat(u, "u", (torch.bfloat16,))
     if g.shape != u.shape:
         raise Dsfp8Error(f"g and u must have the same shape, got {tuple(g.shape)} and {tuple(u.shape)}")
     M, I = g.shape
-    y = torch.empty((M, I), dtype=torch.uint8, device=g.device)
-    s = torch.empty((M, kblocks(I)), dtype=torch.float32, device=g.device)
+    yo, so = out if out is not None else (None, None)
+    y = _out(yo, (M, I), torch.uint8, g.device, "y")
+    s = _out(so, (M, kblocks(I)), torch.float32, g.device, "s")
     h = torch.empty((M, I), dtype=torch.bfloat16, device=g.device) if return_h else None
     st = _lib.load().dsfp8_silu_mul_act_quant(
-        g.data_ptr(), _ld(g), u.data_ptr(), _ld(u), M, I, y.data_ptr(), I, s.data_ptr(), kblocks(I),
+        g.data_ptr(), _ld(g), u.data_ptr(), _ld(u), M, I, y.data_ptr(), _ld(y), s.data_ptr(), _ld(s),
         h.data_ptr() if h is not None else None, I, _fmt(scale_fmt), _stream(g))
     _check("silu_mul_act_quant", st)
     return (y, s, h) if return_h else (y, s)
@@ -117,21 +131,21 @@ def weight_quant(w, scale_fmt="fp32"):
     return q, S
 
 
-def weight_dequant(q, S):
+def weight_dequant(q, S, out=None):
     """bf16 ``[N, K]`` = e4m3 ``q`` times its 128x128 block scale ``S``."""
     q = _mat(_bytes(q), "w", (torch.uint8,))
     _mat(S, "s", (torch.float32,))
     N, K = q.shape
     if tuple(S.shape) != (kblocks(N), kblocks(K)):
         raise Dsfp8Error(f"scale grid must be {(kblocks(N), kblocks(K))}, got {tuple(S.shape)}")
-    out = torch.empty((N, K), dtype=torch.bfloat16, device=q.device)
-    st = _lib.load().dsfp8_weight_dequant(q.data_ptr(), N, K, _ld(q), S.data_ptr(), _ld(S), out.data_ptr(), K,
-                                          _stream(q))
+    out = _out(out, (N, K), torch.bfloat16, q.device, "out")
+    st = _lib.load().dsfp8_weight_dequant(q.data_ptr(), N, K, _ld(q), S.data_ptr(), _ld(S), out.data_ptr(),
+                                          _ld(out), _stream(q))
     _check("weight_dequant", st)
     return out
 
 
-def gemm(a, a_s, b, b_s):
+def gemm(a, a_s, b, b_s, out=None):
     """bf16 ``C [M, N] = A W^T`` with per-K-block scales (A e4m3 [M,K], W e4m3 [N,K])."""
     a = _mat(_bytes(a), "a", (torch.uint8,))
     b = _mat(_bytes(b), "b", (torch.uint8,))
@@ -144,17 +158,17 @@ def gemm(a, a_s, b, b_s):
     if tuple(a_s.shape) != (M, kblocks(K)) or tuple(b_s.shape) != (kblocks(N), kblocks(K)):
         raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and b_s [ceil(N/128), ceil(K/128)]")
     lib = _lib.load()
-    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    c = _out(out, (M, N), torch.bfloat16, a.device, "out")
     wsb = lib.dsfp8_gemm_workspace_bytes(M, N, K)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device) if wsb else None
     st = lib.dsfp8_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), _ld(a_s), b.data_ptr(), _ld(b), b_s.data_ptr(),
-                        _ld(b_s), c.data_ptr(), N, M, N, K, ws.data_ptr() if ws is not None else None, wsb,
+                        _ld(b_s), c.data_ptr(), _ld(c), M, N, K, ws.data_ptr() if ws is not None else None, wsb,
                         _stream(a))
     _check("gemm", st)
     return c
 
 
-def grouped_gemm(a, a_s, b, b_s, offsets):
+def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None):
     """Per-expert product over row ranges: rows ``offsets[e]:offsets[e+1]`` of A use W[e].
 
     ``b`` is e4m3 ``[E, N, K]``, ``b_s`` fp32 ``[E, ceil(N/128), ceil(K/128)]``,
@@ -175,11 +189,12 @@ def grouped_gemm(a, a_s, b, b_s, offsets):
     if tuple(b_s.shape) != (E, kblocks(N), kblocks(K)) or tuple(a_s.shape) != (M, kblocks(K)):
         raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and b_s [E, ceil(N/128), ceil(K/128)]")
     lib = _lib.load()
-    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    c = _out(out, (M, N), torch.bfloat16, a.device, "out")
     wsb = lib.dsfp8_grouped_gemm_workspace_bytes(E, M, N, K)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
     st = lib.dsfp8_grouped_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), _ld(a_s), b.data_ptr(), K, b_s.data_ptr(),
-                                kblocks(K), offsets.data_ptr(), E, M, N, K, c.data_ptr(), N, ws.data_ptr(), wsb,
-                                _stream(a))
+                                kblocks(K), offsets.data_ptr(), E, M, N, K, c.data_ptr(), _ld(c),
+                                workspace.data_ptr(), workspace.numel(), _stream(a))
     _check("grouped_gemm", st)
     return c
