@@ -91,10 +91,10 @@ def setup_dense(dev):
     bufs = dict(
         x=x, q13=q13, s13=s13, q2=q2, s2=s2,
         xq=torch.empty((M, D), dtype=torch.uint8, device=dev),
-        xs=torch.empty((M, kb(D)), dtype=torch.float32, device=dev),
+        xs=ds.new_scales(M, kb(D), dev),
         h13=torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev),
         hq=torch.empty((M, F), dtype=torch.uint8, device=dev),
-        hs=torch.empty((M, kb(F)), dtype=torch.float32, device=dev),
+        hs=ds.new_scales(M, kb(F), dev),
         out=torch.empty((M, D), dtype=torch.bfloat16, device=dev),
     )
     torch.cuda.synchronize()
@@ -144,10 +144,10 @@ def bench_moe(dev, iters):
     del w, q, s
     offd = torch.from_numpy(off).to(dev)
     xq = torch.empty((M, D), dtype=torch.uint8, device=dev)
-    xs = torch.empty((M, kb(D)), dtype=torch.float32, device=dev)
+    xs = ds.new_scales(M, kb(D), dev)
     h13 = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
     hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
-    hs = torch.empty((M, kb(F)), dtype=torch.float32, device=dev)
+    hs = ds.new_scales(M, kb(F), dev)
     out = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(ds._lib.load().dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
     T = Timer()
@@ -221,7 +221,7 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
         ws.append(ds.weight_quant(w, fmt))
     del w
     xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    xs = torch.empty((M, kb(K)), dtype=torch.float32, device=dev)
+    xs = ds.new_scales(M, kb(K), dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     T = Timer()
     for i in range(copies + 3):

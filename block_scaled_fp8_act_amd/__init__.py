@@ -5,7 +5,10 @@ dtypes, allocates its outputs with torch on the input's device, and calls the
 C entry point of the same name on torch's current stream; every step of the
 computation runs in the library's HIP kernels.  e4m3 tensors are exchanged as
 ``torch.uint8`` (``torch.float8_e4m3fn`` inputs are accepted and viewed as
-bytes).  Scales are ``torch.float32``.
+bytes).  Scales are ``torch.float32``.  Activation scales are indexed
+``[M, ceil(K/128)]`` as on the pages; the quantisers return them stored
+K-block-major (a transposed view, strides ``(1, M)``), which is the layout the
+products read fastest, and the products accept either storage order.
 
 The operations follow the DeepSeek-V3 inference kernels as described in the
 "DeepSeek-V3 Administrator & Developer Guide" (sections 6.3, 6.4, 8.5) and the
@@ -68,6 +71,25 @@ def _ld(t):
     return t.stride(-2) if t.numel() > 0 else t.shape[-1]
 
 
+def _scale_strides(t):
+    """(row stride, K-block stride) of an activation-scale matrix [M, KB]."""
+    M, KB = t.shape
+    rs = t.stride(0) if M > 1 else (1 if KB <= 1 or t.stride(1) != 1 else KB)
+    ks = t.stride(1) if KB > 1 else (1 if M <= 1 or t.stride(0) != 1 else M)
+    return rs, ks
+
+
+def _scale_matrix(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or t.dim() != 2:
+        raise Dsfp8Error(f"{name} must be a 2-D float32 CUDA tensor")
+    return _scale_strides(t)
+
+
+def new_scales(M, KB, device):
+    """An activation-scale matrix [M, KB] stored K-block-major (strides (1, M))."""
+    return torch.empty((KB, M), dtype=torch.float32, device=device).t()
+
+
 def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -81,18 +103,29 @@ def _out(out, shape, dtype, device, name):
     return _bytes(out)
 
 
+def _scales_out(out, M, KB, device):
+    if out is None:
+        return new_scales(M, KB, device)
+    if tuple(out.shape) != (M, KB) or out.device != device:
+        raise Dsfp8Error(f"s must be {(M, KB)} on {device}, got {tuple(out.shape)} on {out.device}")
+    _scale_matrix(out, "s")
+    return out
+
+
 def act_quant(x, scale_fmt="fp32", out=None):
     """Quantise bf16 ``x [M, K]`` per row and per 128 columns.
 
     Returns ``(y uint8 [M, K], s float32 [M, ceil(K/128)])`` with x ~= e4m3(y) * s.
-    ``out`` may supply preallocated ``(y, s)`` (row strides are honoured).
+    ``out`` may supply preallocated ``(y, s)`` (row strides are honoured; s
+    may be row-major or K-block-major).
     """
     _mat(x, "x", (torch.bfloat16,))
     M, K = x.shape
     yo, so = out if out is not None else (None, None)
     y = _out(yo, (M, K), torch.uint8, x.device, "y")
-    s = _out(so, (M, kblocks(K)), torch.float32, x.device, "s")
-    st = _lib.load().dsfp8_act_quant(x.data_ptr(), M, K, _ld(x), y.data_ptr(), _ld(y), s.data_ptr(), _ld(s),
+    s = _scales_out(so, M, kblocks(K), x.device)
+    srs, sks = _scale_strides(s)
+    st = _lib.load().dsfp8_act_quant(x.data_ptr(), M, K, _ld(x), y.data_ptr(), _ld(y), s.data_ptr(), srs, sks,
                                      _fmt(scale_fmt), _stream(x))
     _check("act_quant", st)
     return y, s
@@ -109,10 +142,11 @@ def silu_mul_act_quant(g, u, scale_fmt="fp32", return_h=False, out=None):
     M, I = g.shape
     yo, so = out if out is not None else (None, None)
     y = _out(yo, (M, I), torch.uint8, g.device, "y")
-    s = _out(so, (M, kblocks(I)), torch.float32, g.device, "s")
+    s = _scales_out(so, M, kblocks(I), g.device)
+    srs, sks = _scale_strides(s)
     h = torch.empty((M, I), dtype=torch.bfloat16, device=g.device) if return_h else None
     st = _lib.load().dsfp8_silu_mul_act_quant(
-        g.data_ptr(), _ld(g), u.data_ptr(), _ld(u), M, I, y.data_ptr(), _ld(y), s.data_ptr(), _ld(s),
+        g.data_ptr(), _ld(g), u.data_ptr(), _ld(u), M, I, y.data_ptr(), _ld(y), s.data_ptr(), srs, sks,
         h.data_ptr() if h is not None else None, I, _fmt(scale_fmt), _stream(g))
     _check("silu_mul_act_quant", st)
     return (y, s, h) if return_h else (y, s)
@@ -149,7 +183,7 @@ def gemm(a, a_s, b, b_s, out=None):
     """bf16 ``C [M, N] = A W^T`` with per-K-block scales (A e4m3 [M,K], W e4m3 [N,K])."""
     a = _mat(_bytes(a), "a", (torch.uint8,))
     b = _mat(_bytes(b), "b", (torch.uint8,))
-    _mat(a_s, "a_s", (torch.float32,))
+    ars, aks = _scale_matrix(a_s, "a_s")
     _mat(b_s, "b_s", (torch.float32,))
     M, K = a.shape
     N, K2 = b.shape
@@ -161,7 +195,7 @@ def gemm(a, a_s, b, b_s, out=None):
     c = _out(out, (M, N), torch.bfloat16, a.device, "out")
     wsb = lib.dsfp8_gemm_workspace_bytes(M, N, K)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device) if wsb else None
-    st = lib.dsfp8_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), _ld(a_s), b.data_ptr(), _ld(b), b_s.data_ptr(),
+    st = lib.dsfp8_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, b.data_ptr(), _ld(b), b_s.data_ptr(),
                         _ld(b_s), c.data_ptr(), _ld(c), M, N, K, ws.data_ptr() if ws is not None else None, wsb,
                         _stream(a))
     _check("gemm", st)
@@ -176,7 +210,7 @@ def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None):
     """
     a = _mat(_bytes(a), "a", (torch.uint8,))
     b = _mat(_bytes(b), "b", (torch.uint8,), dim=3)
-    _mat(a_s, "a_s", (torch.float32,))
+    ars, aks = _scale_matrix(a_s, "a_s")
     _mat(b_s, "b_s", (torch.float32,), dim=3)
     if not offsets.is_cuda or offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
         raise Dsfp8Error("offsets must be a contiguous int32 CUDA tensor of length E+1")
@@ -193,7 +227,7 @@ def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None):
     wsb = lib.dsfp8_grouped_gemm_workspace_bytes(E, M, N, K)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
-    st = lib.dsfp8_grouped_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), _ld(a_s), b.data_ptr(), K, b_s.data_ptr(),
+    st = lib.dsfp8_grouped_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, b.data_ptr(), K, b_s.data_ptr(),
                                 kblocks(K), offsets.data_ptr(), E, M, N, K, c.data_ptr(), _ld(c),
                                 workspace.data_ptr(), workspace.numel(), _stream(a))
     _check("grouped_gemm", st)

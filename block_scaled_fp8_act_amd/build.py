@@ -31,6 +31,9 @@ DEVICE = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the GEMMs rescale every MFMA result on the VALU,
+    # which cannot read AGPRs directly.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

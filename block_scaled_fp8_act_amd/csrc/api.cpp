@@ -49,9 +49,30 @@ inline dsfp8_status check_mat(const void* p, int64_t rows, int64_t cols, int64_t
 
 inline dsfp8_status launched(hipError_t e) { return e == hipSuccess ? DSFP8_OK : DSFP8_ERR_LAUNCH; }
 
-dsfp8_status check_quant_out(int64_t M, int64_t K, void* y, int64_t ldy, float* s, int64_t lds) {
+// An activation-scale matrix: rows x kbs fp32 values, element (m, b) at
+// p[m * rs + b * ks].  Accepted layouts are row-major (ks == 1, rs >= kbs) and
+// K-block-major (rs == 1, ks >= rows); with a single row or K-block only the
+// other stride matters.
+dsfp8_status check_scales(const void* p, int64_t rows, int64_t kbs, int64_t rs, int64_t ks) {
+  const int64_t kBig = (int64_t)1 << 40;
+  if (rs < 0 || ks < 0 || rs >= kBig || ks >= kBig) return DSFP8_ERR_LD;
+  if (rows > 1 && kbs > 1) {
+    const bool row_major = ks == 1 && rs >= kbs;
+    const bool kb_major = rs == 1 && ks >= rows;
+    if (!row_major && !kb_major) return DSFP8_ERR_LD;
+  } else if (rows > 1) {
+    if (rs < 1) return DSFP8_ERR_LD;
+  } else if (kbs > 1) {
+    if (ks < 1) return DSFP8_ERR_LD;
+  }
+  if (rows > 0 && kbs > 0 && p == nullptr) return DSFP8_ERR_NULL;
+  if (p != nullptr && !al(p, 4)) return DSFP8_ERR_ALIGN;
+  return DSFP8_OK;
+}
+
+dsfp8_status check_quant_out(int64_t M, int64_t K, void* y, int64_t ldy, float* s, int64_t srs, int64_t sks) {
   DSFP8_TRY(check_mat(y, M, K, ldy, 1));
-  DSFP8_TRY(check_mat(s, M, nblk(K), lds, 4));
+  DSFP8_TRY(check_scales(s, M, nblk(K), srs, sks));
   return DSFP8_OK;
 }
 
@@ -77,11 +98,11 @@ const char* dsfp8_status_string(dsfp8_status st) {
 }
 
 dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, void* y, int64_t ldy, float* s,
-                             int64_t lds, int scale_fmt, hipStream_t stream) {
+                             int64_t s_row_stride, int64_t s_kb_stride, int scale_fmt, hipStream_t stream) {
   if (!dim_ok(M) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
   if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
   DSFP8_TRY(check_mat(x, M, K, ldx, 2));
-  DSFP8_TRY(check_quant_out(M, K, y, ldy, s, lds));
+  DSFP8_TRY(check_quant_out(M, K, y, ldy, s, s_row_stride, s_kb_stride));
   dsfp8::ActQuantArgs a{};
   a.g = static_cast<const uint16_t*>(x);
   a.ldg = ldx;
@@ -92,7 +113,8 @@ dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, v
   a.y = static_cast<uint8_t*>(y);
   a.ldy = ldy;
   a.s = s;
-  a.lds = lds;
+  a.s_rs = s_row_stride;
+  a.s_ks = s_kb_stride;
   a.h = nullptr;
   a.ldh = 0;
   a.ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
@@ -100,13 +122,13 @@ dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, v
 }
 
 dsfp8_status dsfp8_silu_mul_act_quant(const void* g, int64_t ldg, const void* u, int64_t ldu, int64_t M, int64_t I,
-                                      void* y, int64_t ldy, float* s, int64_t lds, void* h, int64_t ldh,
-                                      int scale_fmt, hipStream_t stream) {
+                                      void* y, int64_t ldy, float* s, int64_t s_row_stride, int64_t s_kb_stride,
+                                      void* h, int64_t ldh, int scale_fmt, hipStream_t stream) {
   if (!dim_ok(M) || !dim_ok(I)) return DSFP8_ERR_SHAPE;
   if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
   DSFP8_TRY(check_mat(g, M, I, ldg, 2));
   DSFP8_TRY(check_mat(u, M, I, ldu, 2));
-  DSFP8_TRY(check_quant_out(M, I, y, ldy, s, lds));
+  DSFP8_TRY(check_quant_out(M, I, y, ldy, s, s_row_stride, s_kb_stride));
   if (h != nullptr) DSFP8_TRY(check_mat(h, M, I, ldh, 2));
   dsfp8::ActQuantArgs a{};
   a.g = static_cast<const uint16_t*>(g);
@@ -118,7 +140,8 @@ dsfp8_status dsfp8_silu_mul_act_quant(const void* g, int64_t ldg, const void* u,
   a.y = static_cast<uint8_t*>(y);
   a.ldy = ldy;
   a.s = s;
-  a.lds = lds;
+  a.s_rs = s_row_stride;
+  a.s_ks = s_kb_stride;
   a.h = static_cast<uint16_t*>(h);
   a.ldh = h ? ldh : 0;
   a.ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
@@ -175,12 +198,12 @@ size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return 0;
 }
 
-dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas, const void* B, int64_t ldb,
-                        const float* b_s, int64_t ldbs, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
+                        const void* B, int64_t ldb, const float* b_s, int64_t ldbs, void* C, int64_t ldc, int64_t M,
+                        int64_t N, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
   DSFP8_TRY(check_mat(A, M, K, lda, 1));
-  DSFP8_TRY(check_mat(a_s, M, nblk(K), ldas, 4));
+  DSFP8_TRY(check_scales(a_s, M, nblk(K), as_row_stride, as_kb_stride));
   DSFP8_TRY(check_mat(B, N, K, ldb, 1));
   DSFP8_TRY(check_mat(b_s, nblk(N), nblk(K), ldbs, 4));
   DSFP8_TRY(check_mat(C, M, N, ldc, 2));
@@ -190,7 +213,8 @@ dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t ld
   a.A = static_cast<const uint8_t*>(A);
   a.lda = lda;
   a.a_s = a_s;
-  a.ldas = ldas;
+  a.as_rs = as_row_stride;
+  a.as_ks = as_kb_stride;
   a.B = static_cast<const uint8_t*>(B);
   a.ldb = ldb;
   a.b_s = b_s;
@@ -211,16 +235,16 @@ size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N,
   return dsfp8::grouped_workspace_bytes(E);
 }
 
-dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas, const void* B,
-                                int64_t ldb, const float* b_s, int64_t ldbs, const int32_t* offsets, int64_t E,
-                                int64_t M_total, int64_t N, int64_t K, void* C, int64_t ldc, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
+                                int64_t as_kb_stride, const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
+                                const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* C,
+                                int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dim_ok(M_total) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
   if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
   if (offsets == nullptr) return DSFP8_ERR_NULL;
   if (!al(offsets, 4)) return DSFP8_ERR_ALIGN;
   DSFP8_TRY(check_mat(A, M_total, K, lda, 1));
-  DSFP8_TRY(check_mat(a_s, M_total, nblk(K), ldas, 4));
+  DSFP8_TRY(check_scales(a_s, M_total, nblk(K), as_row_stride, as_kb_stride));
   // Every expert's weight must exist even when no row is routed to it.
   DSFP8_TRY(check_mat(B, E * N, K, ldb, 1));
   DSFP8_TRY(check_mat(b_s, E * nblk(N), nblk(K), ldbs, 4));
@@ -233,7 +257,8 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   a.A = static_cast<const uint8_t*>(A);
   a.lda = lda;
   a.a_s = a_s;
-  a.ldas = ldas;
+  a.as_rs = as_row_stride;
+  a.as_ks = as_kb_stride;
   a.B = static_cast<const uint8_t*>(B);
   a.ldb = ldb;
   a.b_s = b_s;

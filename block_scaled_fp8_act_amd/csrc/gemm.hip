@@ -82,8 +82,16 @@ __device__ __forceinline__ u32x4 load_chunk(const uint8_t* row, int64_t k, int64
   return v;
 }
 
-// Byte offset of 16-byte chunk c of tile row r in LDS.
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk c of tile row r in LDS.  gfx950's LDS serves
+// 16 lanes x 16 bytes per cycle from 64 four-byte banks, so a 128-byte row
+// covers half of the banks and the row's parity selects the half; XOR-ing the
+// chunk index with (r >> 1) & 7 spreads the 16 rows of an MFMA fragment read
+// over all 64 banks.
+#ifndef DSFP8_SWZ_SHIFT
+#define DSFP8_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int swz_key(int r) { return (r >> DSFP8_SWZ_SHIFT) & 7; }
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ swz_key(r)) << 4); }
 
 // MFMA operand of one 16-row slice: lane (r, g) = (lane % 16, lane / 16) holds
 // K bytes [32g, 32g + 32) of row r.  A and B use the same K assignment, so the
@@ -106,6 +114,47 @@ struct TileRef {
   int64_t row0, row_end; // rows [row0, min(row0 + BM, row_end)) are computed
   int64_t n0;
 };
+
+// Epilogue: round to bf16, stage each wave's WM x WN tile in LDS (which the
+// caller has finished reading), then write rows of C with 16-byte stores.
+template <class CF>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, const v4f (&acc)[CF::TM][CF::TN],
+                                           uint8_t* smem, int wave, int wm, int wn, int lane) {
+  const int fr = lane & 15, fg = lane >> 4;
+  const int64_t N = p.N;
+  constexpr int CS = CF::WN + CF::CPAD;
+  uint16_t* cst = reinterpret_cast<uint16_t*>(smem) + wave * CF::WM * CS;
+#pragma unroll
+  for (int i = 0; i < CF::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const __bf16 h = (__bf16)acc[i][j][v];
+        cst[(i * 16 + 4 * fg + v) * CS + j * 16 + fr] = __builtin_bit_cast(uint16_t, h);
+      }
+  __syncthreads();
+  const int64_t crow0 = t.row0 + wm * CF::WM;
+  const int64_t ccol0 = t.n0 + wn * CF::WN;
+  const int64_t row_lim = t.row_end;
+  const bool cvec = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 8 == 0);
+  constexpr int CPR = CF::WN / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int it = 0; it < CF::WM * CPR / 64; ++it) {
+    const int c = lane + 64 * it;
+    const int r = c / CPR, cc = c % CPR;
+    const int64_t row = crow0 + r;
+    const int64_t col = ccol0 + cc * 8;
+    if (row >= row_lim || col >= N) continue;
+    const uint16_t* src = cst + r * CS + cc * 8;
+    uint16_t* dst = p.C + row * p.ldc + col;
+    if (cvec && col + 8 <= N) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = src[e];
+    }
+  }
+}
 
 template <class CF, int VEC>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
@@ -144,7 +193,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
     }
     if (tid < BM) {
       const int64_t row = t.row0 + tid;
-      rs = row < t.row_end ? t.a_s[row * p.ldas + kb] : 0.0f;
+      rs = row < t.row_end ? t.a_s[row * p.as_rs + (int64_t)kb * p.as_ks] : 0.0f;
     }
   };
   auto lstore = [&](int buf) {
@@ -202,40 +251,218 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
     __syncthreads();
   }
 
-  // Epilogue: round to bf16, stage this wave's WM x WN tile in LDS, then write
-  // rows of C with 16-byte stores.
-  constexpr int CS = CF::WN + CF::CPAD;
-  uint16_t* cst = reinterpret_cast<uint16_t*>(smem) + wave * CF::WM * CS;
+  __syncthreads();
+  store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
+}
+
+// ---- direct-to-LDS pipeline (16-byte aligned operands) --------------------------------
+//
+// Each stage of a STAGES-deep LDS ring holds one K-block: BM rows of A, BN rows
+// of B (128 bytes each, in the same swizzled layout as above) and the BM
+// activation scales.  Stages are filled with buffer_load_dwordx4 ... lds, which
+// writes a wavefront's 64 x 16 bytes straight into LDS without passing through
+// VGPRs; the swizzle is applied on the global side (the lane that lands on LDS
+// chunk p fetches the logical chunk stored there).  The buffer descriptors
+// start at the tile's first row and end after its last valid row, so rows past
+// the matrix edge read as zero without a branch; a chunk past K is sent to an
+// out-of-range offset for the same effect.  One barrier per K-block: after it,
+// stage kb is complete for every wave and stage kb-1 is no longer read, so the
+// loads of K-block kb+STAGES-1 are issued into it before the MFMAs of kb.
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The loads are issued from inline assembly so that the compiler, which
+// cannot tell the stages of the ring apart, does not add a vmcnt(0) wait in
+// front of every LDS read; the kernel waits for each stage itself.  M0 holds
+// the wave's LDS destination and is set in the same statement; the s_nop
+// provides the wait state required between an SALU write of M0 and an LDS
+// DMA that reads it.  Nothing else in these kernels uses M0 (no LDS DMA by
+// the compiler, no indexed register access), so the value need not survive.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Per-lane 64-bit addresses: each active lane fetches one dword from anywhere.
+__device__ __forceinline__ void dma_gather_b32(uint32_t lds, const float* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds), "v"(addr)
+               : "memory");
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // above every descriptor's size
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct DmaCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  // Scale area of a stage: one slot of SA_ROWS + 4 floats per wave holding the
+  // activation scales of the rows that wave fetches, then (at index SA_ROWS)
+  // the weight scale of the wave's own 128-column block.
+  static constexpr int SA_ROWS = BM / NW;
+  static constexpr int SAW = SA_ROWS + 4;
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  static constexpr int S_OFF = A_BYTES + B_BYTES;
+  static constexpr int STAGE_BYTES = S_OFF + NW * SAW * 4;
+  static constexpr int A_INSTR = A_BYTES / 1024 / NW;   // 1 KB (8 rows) per wave instruction
+  static constexpr int B_INSTR = B_BYTES / 1024 / NW;
+  static constexpr int LOADS = A_INSTR + B_INSTR + 1;    // vector-memory instructions per stage and wave
+  static constexpr int CPAD = 8;
+  static constexpr int C_BYTES = NW * WM * (WN + CPAD) * 2;
+  static constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int LDS_BYTES = MAIN_BYTES > C_BYTES ? MAIN_BYTES : C_BYTES;
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole 1 KB segments per wave");
+  static_assert(SA_ROWS >= 4 && SA_ROWS % 4 == 0 && SA_ROWS < 64 && BM % NW == 0, "scale rows per wave");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-block");
+  static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
+};
+
+#ifndef DSFP8_DMA_TILE
+#define DSFP8_DMA_TILE 128, 128, 2, 2, 2
+#endif
+using CfgDma = DmaCfg<DSFP8_DMA_TILE>;
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0: raw buffer
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <class CF>
+__device__ __forceinline__ void wait_stage(int later) {
+  // `later` = number of stages issued after the one waited for (0..STAGES-2).
+  if constexpr (CF::STAGES >= 4) {
+    if (later >= 2) { wait_vmcnt<CF::LOADS * 2>(); return; }
+  }
+  if constexpr (CF::STAGES >= 3) {
+    if (later >= 1) { wait_vmcnt<CF::LOADS>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <class CF>
+__device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
+  constexpr int NW = CF::NW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int64_t K = p.K, N = p.N;
+  const int nkb = (int)((K + BK - 1) / BK);
+  const int64_t kbn = (N + BK - 1) / BK;
+
+  const int64_t rowsA = t.row_end - t.row0 < CF::BM ? t.row_end - t.row0 : CF::BM;
+  const int64_t rowsB = N - t.n0 < CF::BN ? N - t.n0 : CF::BN;
+  const i32x4 rsA = make_rsrc(t.A + t.row0 * p.lda, (uint32_t)(rowsA * p.lda));
+  const i32x4 rsB = make_rsrc(t.B + t.n0 * p.ldb, (uint32_t)(rowsB * p.ldb));
+  // The weight-scale row of this wave's 128-column block (clamped for waves
+  // past the last column, whose results are never stored).
+  int64_t nbi = (t.n0 + wn * CF::WN) / BK;
+  if (nbi > kbn - 1) nbi = kbn - 1;
+  // Scale gather: lane l < SA_ROWS fetches a_s of tile row wave*SA_ROWS + l,
+  // lane SA_ROWS fetches b_s[nbi, kb]; K-block kb adds kb * stride.
+  const int srow = wave * CF::SA_ROWS + lane;
+  const bool s_act = lane < CF::SA_ROWS ? srow < rowsA : lane == CF::SA_ROWS;
+  const float* sbase = lane < CF::SA_ROWS ? t.a_s + (t.row0 + srow) * p.as_rs : t.b_s + nbi * p.ldbs;
+  const int64_t sstep = lane < CF::SA_ROWS ? p.as_ks : 1;
+
+  // Per-lane source offsets (K-block independent): lane -> LDS chunk (row r,
+  // physical chunk lane % 8) <- logical chunk c of row r.
+  uint32_t offA[CF::A_INSTR], offB[CF::B_INSTR];
+  int kcA[CF::A_INSTR], kcB[CF::B_INSTR];
+#pragma unroll
+  for (int i = 0; i < CF::A_INSTR; ++i) {
+    const int r = (wave + NW * i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_key(r);
+    offA[i] = (uint32_t)(r * p.lda + c * 16);
+    kcA[i] = c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < CF::B_INSTR; ++i) {
+    const int r = (wave + NW * i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_key(r);
+    offB[i] = (uint32_t)(r * p.ldb + c * 16);
+    kcB[i] = c * 16;
+  }
+
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
+  auto issue = [&](int kb, int stage) {
+    const uint32_t st = lds0 + (uint32_t)(stage * CF::STAGE_BYTES);
+    const int64_t kbyte = (int64_t)kb * BK;
+#pragma unroll
+    for (int i = 0; i < CF::A_INSTR; ++i) {
+      const uint32_t off = (kbyte + kcA[i] < K) ? offA[i] + (uint32_t)kbyte : kOob;
+      dma_b128(rsA, st + (uint32_t)((wave + NW * i) * 1024), off);
+    }
+#pragma unroll
+    for (int i = 0; i < CF::B_INSTR; ++i) {
+      const uint32_t off = (kbyte + kcB[i] < K) ? offB[i] + (uint32_t)kbyte : kOob;
+      dma_b128(rsB, st + (uint32_t)(CF::A_BYTES + (wave + NW * i) * 1024), off);
+    }
+    if (s_act) dma_gather_b32(st + (uint32_t)(CF::S_OFF + wave * CF::SAW * 4), sbase + (int64_t)kb * sstep);
+  };
+
+  v4f acc[CF::TM][CF::TN];
 #pragma unroll
   for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::TN; ++j)
+    for (int j = 0; j < CF::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const __bf16 h = (__bf16)acc[i][j][v];
-        cst[(i * 16 + 4 * fg + v) * CS + j * 16 + fr] = __builtin_bit_cast(uint16_t, h);
+  for (int s = 0; s < CF::STAGES - 1; ++s)
+    if (s < nkb) issue(s, s);
+
+  const int fr = lane & 15, fg = lane >> 4;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int later = (nkb - 1 - kb) < (CF::STAGES - 2) ? (nkb - 1 - kb) : (CF::STAGES - 2);
+    wait_stage<CF>(later);
+    __syncthreads();
+    if (kb + CF::STAGES - 1 < nkb) issue(kb + CF::STAGES - 1, (kb + CF::STAGES - 1) % CF::STAGES);
+    const uint8_t* st = smem + (kb % CF::STAGES) * CF::STAGE_BYTES;
+    const float* sarea = reinterpret_cast<const float*>(st + CF::S_OFF);
+    const float bsv = sarea[wave * CF::SAW + CF::SA_ROWS];
+    const uint8_t* at = st;
+    const uint8_t* bt = st + CF::A_BYTES;
+    v8i bfr[CF::TN];
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j) bfr[j] = read_frag(bt, wn * CF::WN + j * 16 + fr, fg);
+#pragma unroll
+    for (int i = 0; i < CF::TM; ++i) {
+      const v8i afr = read_frag(at, wm * CF::WM + i * 16 + fr, fg);
+      const int srow4 = wm * CF::WM + i * 16 + 4 * fg;  // first of this lane's 4 rows
+      const v4f sc = *reinterpret_cast<const v4f*>(sarea + (srow4 / CF::SA_ROWS) * CF::SAW + srow4 % CF::SA_ROWS) * bsv;
+#pragma unroll
+      for (int j = 0; j < CF::TN; ++j) {
+        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc[v], acc[i][j][v]);
       }
-  __syncthreads();
-  const int64_t crow0 = t.row0 + wm * CF::WM;
-  const int64_t ccol0 = t.n0 + wn * CF::WN;
-  const int64_t row_lim = t.row_end;
-  const bool cvec = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 8 == 0);
-  constexpr int CPR = CF::WN / 8;  // 16-byte chunks per staged row
-#pragma unroll
-  for (int it = 0; it < CF::WM * CPR / 64; ++it) {
-    const int c = lane + 64 * it;
-    const int r = c / CPR, cc = c % CPR;
-    const int64_t row = crow0 + r;
-    const int64_t col = ccol0 + cc * 8;
-    if (row >= row_lim || col >= N) continue;
-    const uint16_t* src = cst + r * CS + cc * 8;
-    uint16_t* dst = p.C + row * p.ldc + col;
-    if (cvec && col + 8 <= N) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = src[e];
     }
   }
+  __syncthreads();
+  store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
 }
 
 // Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges, then
@@ -254,6 +481,14 @@ __device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t ti
   tn = in / gsize;
 }
 
+// VEC > 0: the register-staged pipeline with VEC-byte loads (any alignment);
+// VEC == 0: the direct-to-LDS pipeline (16-byte aligned operands, K % 16 == 0).
+template <class CF, int VEC>
+__device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
+  if constexpr (VEC == 0) gemm_tile_dma<CF>(p, t, smem);
+  else gemm_tile<CF, VEC>(p, t, smem);
+}
+
 template <class CF, int VEC>
 __global__ __launch_bounds__(CF::kThreads) void gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
@@ -269,7 +504,7 @@ __global__ __launch_bounds__(CF::kThreads) void gemm_kernel(GemmArgs p) {
   t.row0 = tm * CF::BM;
   t.row_end = p.M;
   t.n0 = tn * CF::BN;
-  gemm_tile<CF, VEC>(p, t, smem);
+  run_tile<CF, VEC>(p, t, smem);
 }
 
 // Expert row range [lo, hi) with every bound clamped into [0, M_total].
@@ -332,68 +567,88 @@ __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) 
   int64_t r0, r1;
   expert_rows(p.offsets, e, p.M, r0, r1);
   const int64_t kbn = (p.N + BK - 1) / BK;
-  const int64_t kbk = (p.K + BK - 1) / BK;
   TileRef t;
   t.A = p.A;
   t.a_s = p.a_s;
   t.B = p.B + e * p.N * p.ldb;
   t.b_s = p.b_s + e * kbn * p.ldbs;
-  (void)kbk;
   t.row0 = r0 + (slot - ts[e]) * CF::BM;
   t.row_end = r1;
   t.n0 = (int64_t)blockIdx.y * CF::BN;
-  gemm_tile<CF, VEC>(p, t, smem);
+  run_tile<CF, VEC>(p, t, smem);
 }
 
 inline bool aligned(const void* q, size_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; }
 
-// Widest load width (bytes) valid for every row start of A and B and for K.
+// Load width for the operands: 0 selects the direct-to-LDS pipeline, which
+// needs 16-byte aligned rows, K % 16 == 0 and 32-bit tile offsets; otherwise
+// the widest aligned width for the register-staged pipeline.
+template <class CF>
 int pick_vec(const GemmArgs& a) {
+  if (a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16) &&
+      (int64_t)CF::BM * a.lda < ((int64_t)1 << 31) && (int64_t)CF::BN * a.ldb < ((int64_t)1 << 31) &&
+      true)
+    return 0;
   const int cands[3] = {16, 8, 4};
   for (int v : cands)
     if (a.K % v == 0 && a.lda % v == 0 && a.ldb % v == 0 && aligned(a.A, v) && aligned(a.B, v)) return v;
   return 1;
 }
 
-template <class CF>
-hipError_t launch_dense(const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles = ((a.M + CF::BM - 1) / CF::BM) * ((a.N + CF::BN - 1) / CF::BN);
-  dim3 g((unsigned)tiles), b(CF::kThreads);
-  switch (pick_vec(a)) {
-    case 16: hipLaunchKernelGGL((gemm_kernel<CF, 16>), g, b, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((gemm_kernel<CF, 8>), g, b, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<CF, 4>), g, b, 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<CF, 1>), g, b, 0, s, a); break;
+#define DSFP8_LAUNCH(KERN, CF, VEC, GRID) hipLaunchKernelGGL((KERN<CF, VEC>), GRID, dim3(CF::kThreads), 0, s, a)
+
+template <class CFD, class CFG, bool GROUPED>
+hipError_t dispatch(const GemmArgs& a, dim3 gd, dim3 gg, hipStream_t s) {
+  switch (pick_vec<CFD>(a)) {
+    case 0:
+      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFD, 0, gd);
+      else DSFP8_LAUNCH(gemm_kernel, CFD, 0, gd);
+      break;
+    case 16:
+      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFG, 16, gg);
+      else DSFP8_LAUNCH(gemm_kernel, CFG, 16, gg);
+      break;
+    case 8:
+      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFG, 8, gg);
+      else DSFP8_LAUNCH(gemm_kernel, CFG, 8, gg);
+      break;
+    case 4:
+      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFG, 4, gg);
+      else DSFP8_LAUNCH(gemm_kernel, CFG, 4, gg);
+      break;
+    default:
+      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFG, 1, gg);
+      else DSFP8_LAUNCH(gemm_kernel, CFG, 1, gg);
+      break;
   }
   return hipGetLastError();
 }
 
 template <class CF>
-hipError_t launch_grouped(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.M, CF::BM, a.tile_start);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int64_t slots = (a.M + CF::BM - 1) / CF::BM + a.E;
-  dim3 g((unsigned)slots, (unsigned)((a.N + CF::BN - 1) / CF::BN)), b(CF::kThreads);
-  switch (pick_vec(a)) {
-    case 16: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 16>), g, b, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 8>), g, b, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 4>), g, b, 0, s, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_kernel<CF, 1>), g, b, 0, s, a); break;
-  }
-  return hipGetLastError();
+dim3 dense_grid(const GemmArgs& a) {
+  return dim3((unsigned)(((a.M + CF::BM - 1) / CF::BM) * ((a.N + CF::BN - 1) / CF::BN)));
+}
+
+template <class CF>
+dim3 grouped_grid(const GemmArgs& a) {
+  return dim3((unsigned)((a.M + CF::BM - 1) / CF::BM + a.E), (unsigned)((a.N + CF::BN - 1) / CF::BN));
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  return launch_dense<Cfg128>(a, stream);
+  return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.M == 0) return hipSuccess;
-  return launch_grouped<Cfg128>(a, stream);
+  // The tile schedule depends on the row-tile height of the pipeline used.
+  const int bm = pick_vec<CfgDma>(a) == 0 ? CfgDma::BM : Cfg128::BM;
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.E, a.M, bm, a.tile_start);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return dispatch<CfgDma, Cfg128, true>(a, grouped_grid<CfgDma>(a), grouped_grid<Cfg128>(a), stream);
 }
 
 size_t grouped_workspace_bytes(int64_t E) {

@@ -17,7 +17,7 @@ struct ActQuantArgs {
   uint8_t* y;
   int64_t ldy;
   float* s;
-  int64_t lds;
+  int64_t s_rs, s_ks;  // scale (m, b) at s[m * s_rs + b * s_ks]
   uint16_t* h;        // optional bf16 output of SiLU(g)*u
   int64_t ldh;
   bool ue8m0;
@@ -47,7 +47,7 @@ struct GemmArgs {
   const uint8_t* A;
   int64_t lda;
   const float* a_s;
-  int64_t ldas;
+  int64_t as_rs, as_ks;  // activation scale (m, b) at a_s[m * as_rs + b * as_ks]
   const uint8_t* B;
   int64_t ldb;
   const float* b_s;

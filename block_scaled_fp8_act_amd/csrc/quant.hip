@@ -66,7 +66,7 @@ __device__ __forceinline__ void quantise_unit(const float (&v)[8], int nvalid, c
     for (int j = 0; j < 8; ++j)
       if (j < nvalid) yrow[col + j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xff);
   }
-  if (lane16 == 0) a.s[m * a.lds + b] = s;
+  if (lane16 == 0) a.s[m * a.s_rs + b * a.s_ks] = s;
 }
 
 // Load this lane's 8 bf16 values of one unit.  VEC: one 16-byte load (the

@@ -22,7 +22,12 @@
  *   Matrices are row-major with the innermost dimension contiguous; "ld" is the
  *   row stride in ELEMENTS and must be >= the row length.  Block size is fixed
  *   at 128 ([DS] item 10: weight_block_size [128, 128]).  KB(K) = ceil(K/128).
- *   Activation scales: fp32 [M, KB(K)], row stride lds (elements).
+ *   Activation scales: fp32, logically [M, KB(K)]; element (m, b) is stored
+ *     at s[m * s_row_stride + b * s_kb_stride].  Row-major storage has
+ *     s_kb_stride = 1, s_row_stride >= KB(K); K-block-major ("column-major")
+ *     storage has s_row_stride = 1, s_kb_stride >= M.  The products read a
+ *     K-block's scales for consecutive rows with one coalesced access when
+ *     they are K-block-major, which is the layout to prefer.
  *   Weight scales:     fp32 [KB(N), KB(K)], row stride in elements.
  *   A last block narrower than 128 (K or N not a multiple of 128) is treated
  *   as zero-padded to 128 ([DS] item 3); only its real elements are read or
@@ -53,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSFP8_ABI_VERSION 1
+#define DSFP8_ABI_VERSION 2
 #define DSFP8_BLOCK 128
 
 typedef int dsfp8_status;
@@ -97,14 +102,16 @@ const char* dsfp8_status_string(dsfp8_status status);
  *
  *   x      bf16 [M, K], row stride ldx >= K            (device, read)
  *   y      e4m3 [M, K], row stride ldy >= K            (device, written)
- *   s      fp32 [M, KB(K)], row stride lds >= KB(K)    (device, written)
+ *   s      fp32 [M, KB(K)], strides s_row_stride, s_kb_stride (see above)
+ *                                                      (device, written)
  * K need not be a multiple of 128 (the pages' assertion that it is is relaxed;
  * the partial block follows the zero-padding rule).
  * Errors: NULL (x/y/s NULL with M*K > 0), SHAPE (M or K < 0), LD, ALIGN (x not
  * 2-byte or s not 4-byte aligned), SCALE_FMT, LAUNCH.
  */
 dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx,
-                             void* y, int64_t ldy, float* s, int64_t lds,
+                             void* y, int64_t ldy,
+                             float* s, int64_t s_row_stride, int64_t s_kb_stride,
                              int scale_fmt, hipStream_t stream);
 
 /*
@@ -118,7 +125,7 @@ dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx,
  *   g, u   bf16 [M, I], row strides ldg, ldu >= I  (device, read; g and u may be
  *          the two halves of one [M, 2I] product, e.g. u = g + I, ldg = ldu = 2I)
  *   y      e4m3 [M, I], row stride ldy             (device, written)
- *   s      fp32 [M, KB(I)], row stride lds         (device, written)
+ *   s      fp32 [M, KB(I)], strides as act_quant   (device, written)
  *   h      bf16 [M, I], row stride ldh, or NULL    (device, written if not NULL)
  * The exponential is the hardware's, so h is reproducible only to within one
  * bf16 unit in the last place of a correctly rounded evaluation; (y, s) are
@@ -128,7 +135,8 @@ dsfp8_status dsfp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx,
 dsfp8_status dsfp8_silu_mul_act_quant(const void* g, int64_t ldg,
                                       const void* u, int64_t ldu,
                                       int64_t M, int64_t I,
-                                      void* y, int64_t ldy, float* s, int64_t lds,
+                                      void* y, int64_t ldy,
+                                      float* s, int64_t s_row_stride, int64_t s_kb_stride,
                                       void* h, int64_t ldh,
                                       int scale_fmt, hipStream_t stream);
 
@@ -172,7 +180,8 @@ dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t l
  * accumulated in fp32; the order of accumulation is unspecified.
  *
  *   A      e4m3 [M, K], row stride lda                  (device, read)
- *   a_s    fp32 [M, KB(K)], row stride ldas             (device, read)
+ *   a_s    fp32 [M, KB(K)], strides as_row_stride, as_kb_stride (see
+ *          above; K-block-major is fastest)             (device, read)
  *   B      e4m3 [N, K], row stride ldb (the weight)     (device, read)
  *   b_s    fp32 [KB(N), KB(K)], row stride ldbs         (device, read)
  *   C      bf16 [M, N], row stride ldc                  (device, written)
@@ -180,7 +189,8 @@ dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t l
  *          dsfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
  * Errors: NULL, SHAPE, LD, ALIGN, WORKSPACE, LAUNCH.
  */
-dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas,
+dsfp8_status dsfp8_gemm(const void* A, int64_t lda,
+                        const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
                         const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
                         void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -196,7 +206,8 @@ size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   C[o_e:o_{e+1}] = dsfp8_gemm(A[o_e:o_{e+1}], a_s[o_e:o_{e+1}], B[e], b_s[e])
  *
  *   A        e4m3 [M_total, K], row stride lda              (device, read)
- *   a_s      fp32 [M_total, KB(K)], row stride ldas         (device, read)
+ *   a_s      fp32 [M_total, KB(K)], strides as_row_stride, as_kb_stride
+ *                                                           (device, read)
  *   B        e4m3 [E, N, K]: row stride ldb, expert stride N*ldb       (device)
  *   b_s      fp32 [E, KB(N), KB(K)]: row stride ldbs, expert stride
  *            KB(N)*ldbs                                     (device, read)
@@ -210,7 +221,8 @@ size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * part of this call.
  * Errors: NULL, SHAPE (E < 1, or E > 65536), LD, ALIGN, WORKSPACE, LAUNCH.
  */
-dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t ldas,
+dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda,
+                                const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
                                 const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
                                 const int32_t* offsets, int64_t E, int64_t M_total,
                                 int64_t N, int64_t K, void* C, int64_t ldc,

@@ -32,6 +32,14 @@ def dev_f32(a):
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
 
 
+def dev_scales(a_s, layout):
+    """Activation scales [M, KB] on the device, stored row-major ("row") or
+    K-block-major ("kb", a transposed view with strides (1, M))."""
+    if layout == "row":
+        return dev_f32(a_s)
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a_s, np.float32).T)).cuda().t()
+
+
 def host_bits16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 

@@ -64,28 +64,33 @@ def test_status_codes_match_header():
 
 def test_act_quant_validation(lib):
     f = lib.dsfp8_act_quant
-    assert f(P, -1, 128, 128, P, 128, P, 1, 0, None) == SHAPE
-    assert f(P, 4, 1 << 31, 1 << 31, P, 1 << 31, P, 1 << 24, 0, None) == SHAPE
-    assert f(P, 4, 128, 128, P, 128, P, 1, 2, None) == FMT
-    assert f(None, 4, 128, 128, P, 128, P, 1, 0, None) == NULL
-    assert f(P, 4, 128, 128, None, 128, P, 1, 0, None) == NULL
-    assert f(P, 4, 128, 128, P, 128, None, 1, 0, None) == NULL
-    assert f(P, 4, 128, 100, P, 128, P, 1, 0, None) == LD
-    assert f(P, 4, 128, 128, P, 127, P, 1, 0, None) == LD
-    assert f(P, 4, 200, 200, P, 200, P, 1, 0, None) == LD          # scales need ceil(200/128) = 2
-    assert f(P + 1, 4, 128, 128, P, 128, P, 1, 0, None) == ALIGN    # bf16 needs 2-byte alignment
-    assert f(P, 4, 128, 128, P, 128, P + 2, 1, 0, None) == ALIGN    # fp32 needs 4
+    # x, M, K, ldx, y, ldy, s, s_row_stride, s_kb_stride, fmt, stream
+    assert f(P, -1, 128, 128, P, 128, P, 1, 1, 0, None) == SHAPE
+    assert f(P, 4, 1 << 31, 1 << 31, P, 1 << 31, P, 1 << 24, 1, 0, None) == SHAPE
+    assert f(P, 4, 128, 128, P, 128, P, 1, 1, 2, None) == FMT
+    assert f(None, 4, 128, 128, P, 128, P, 1, 1, 0, None) == NULL
+    assert f(P, 4, 128, 128, None, 128, P, 1, 1, 0, None) == NULL
+    assert f(P, 4, 128, 128, P, 128, None, 1, 1, 0, None) == NULL
+    assert f(P, 4, 128, 100, P, 128, P, 1, 1, 0, None) == LD
+    assert f(P, 4, 128, 128, P, 127, P, 1, 1, 0, None) == LD
+    assert f(P, 4, 256, 256, P, 256, P, 1, 1, 0, None) == LD          # 2 K-blocks overlap
+    assert f(P, 4, 256, 256, P, 256, P, 2, 2, 0, None) == LD          # neither layout
+    assert f(P, 4, 256, 256, P, 256, P, 1, 3, 0, None) == LD          # K-block-major needs ks >= M
+    assert f(P + 1, 4, 128, 128, P, 128, P, 1, 1, 0, None) == ALIGN    # bf16 needs 2-byte alignment
+    assert f(P, 4, 128, 128, P, 128, P + 2, 1, 1, 0, None) == ALIGN    # fp32 needs 4
     # empty problems are valid and launch nothing
-    assert f(None, 0, 128, 128, None, 128, None, 1, 0, None) == OK
-    assert f(None, 5, 0, 0, None, 0, None, 0, 0, None) == OK
+    assert f(None, 0, 128, 128, None, 128, None, 1, 1, 0, None) == OK
+    assert f(None, 5, 0, 0, None, 0, None, 1, 1, 0, None) == OK
 
 
 def test_silu_and_weight_validation(lib):
     f = lib.dsfp8_silu_mul_act_quant
-    assert f(P, 256, P, 256, 4, 256, P, 256, P, 2, None, 0, 9, None) == FMT
-    assert f(P, 256, None, 256, 4, 256, P, 256, P, 2, None, 0, 0, None) == NULL
-    assert f(P, 256, P, 256, 4, 256, P, 256, P, 2, P, 100, 0, None) == LD
-    assert f(None, 256, None, 256, 0, 256, None, 256, None, 2, None, 0, 0, None) == OK
+    # g, ldg, u, ldu, M, I, y, ldy, s, srs, sks, h, ldh, fmt, stream
+    assert f(P, 256, P, 256, 4, 256, P, 256, P, 2, 1, None, 0, 9, None) == FMT
+    assert f(P, 256, None, 256, 4, 256, P, 256, P, 2, 1, None, 0, 0, None) == NULL
+    assert f(P, 256, P, 256, 4, 256, P, 256, P, 2, 1, P, 100, 0, None) == LD
+    assert f(P, 256, P, 256, 4, 256, P, 256, P, 1, 2, None, 0, 0, None) == LD
+    assert f(None, 256, None, 256, 0, 256, None, 256, None, 2, 1, None, 0, 0, None) == OK
     q = lib.dsfp8_weight_quant
     assert q(P, 7, 128, 128, 128, P, 128, P, 1, 0, None) == DTYPE
     assert q(P, 0, 128, 128, 128, P, 128, P, 1, 3, None) == FMT
@@ -100,26 +105,27 @@ def test_silu_and_weight_validation(lib):
 
 def test_gemm_validation(lib):
     g = lib.dsfp8_gemm
-    # A, lda, a_s, ldas, B, ldb, b_s, ldbs, C, ldc, M, N, K, ws, wsb, stream
-    assert g(P, 256, P, 2, P, 256, P, 2, P, 64, -8, 64, 256, None, 0, None) == SHAPE
-    assert g(None, 256, P, 2, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == NULL
-    assert g(P, 255, P, 2, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
-    assert g(P, 256, P, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
-    assert g(P, 256, P, 2, P, 256, P, 2, P, 63, 8, 64, 256, None, 0, None) == LD
-    assert g(P, 256, P + 1, 2, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == ALIGN
-    assert g(P, 256, P, 2, P, 256, P, 2, P + 1, 64, 8, 64, 256, None, 0, None) == ALIGN
+    # A, lda, a_s, as_rs, as_ks, B, ldb, b_s, ldbs, C, ldc, M, N, K, ws, wsb, stream
+    assert g(P, 256, P, 2, 1, P, 256, P, 2, P, 64, -8, 64, 256, None, 0, None) == SHAPE
+    assert g(None, 256, P, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == NULL
+    assert g(P, 255, P, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
+    assert g(P, 256, P, 1, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
+    assert g(P, 256, P, 1, 7, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD   # ks < M
+    assert g(P, 256, P, 2, 1, P, 256, P, 1, P, 64, 8, 64, 256, None, 0, None) == LD   # b_s row too short
+    assert g(P, 256, P, 2, 1, P, 256, P, 2, P, 63, 8, 64, 256, None, 0, None) == LD
+    assert g(P, 256, P + 1, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == ALIGN
+    assert g(P, 256, P, 2, 1, P, 256, P, 2, P + 1, 64, 8, 64, 256, None, 0, None) == ALIGN
     assert lib.dsfp8_gemm_workspace_bytes(4096, 18432, 7168) == 0
 
 
 def test_grouped_validation(lib):
     g = lib.dsfp8_grouped_gemm
-    # A, lda, a_s, ldas, B, ldb, b_s, ldbs, offsets, E, M, N, K, C, ldc, ws, wsb, stream
-    args = [P, 256, P, 2, P, 256, P, 2, P, 4, 100, 64, 256, P, 64, P, 1 << 20, None]
+    names = ["A", "lda", "a_s", "as_rs", "as_ks", "B", "ldb", "b_s", "ldbs", "offsets", "E", "M", "N", "K", "C",
+             "ldc", "ws", "wsb", "stream"]
+    args = [P, 256, P, 1, 100, P, 256, P, 2, P, 4, 100, 64, 256, P, 64, P, 1 << 20, None]
 
     def call(**kw):
         a = list(args)
-        names = ["A", "lda", "a_s", "ldas", "B", "ldb", "b_s", "ldbs", "offsets", "E", "M", "N", "K", "C",
-                 "ldc", "ws", "wsb", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return g(*a)
@@ -130,6 +136,7 @@ def test_grouped_validation(lib):
     assert call(offsets=P + 2) == ALIGN
     assert call(ldb=100) == LD
     assert call(ldbs=1) == LD
+    assert call(as_ks=99) == LD
     need = lib.dsfp8_grouped_gemm_workspace_bytes(4, 100, 64, 256)
     assert need >= 5 * 4
     assert call(wsb=need - 1) == WS

@@ -17,7 +17,7 @@ from oracle import formats as F
 from oracle import gemm as G
 from oracle import quant as Q
 
-from gpu_helpers import (check_gemm_full, check_product, dev_bf16, dev_f32, dev_u8,
+from gpu_helpers import (check_gemm_full, check_product, dev_bf16, dev_f32, dev_scales, dev_u8,
                          host_bits16, host_u8)
 
 pytestmark = pytest.mark.gpu
@@ -30,32 +30,44 @@ def operands(M, N, K, cid, ue8m0=False, outliers=0.0):
     return a, a_s, b, b_s
 
 
-def run(a, a_s, b, b_s):
-    c = ds.gemm(dev_u8(a), dev_f32(a_s), dev_u8(b), dev_f32(b_s))
+def run(a, a_s, b, b_s, layout="kb"):
+    c = ds.gemm(dev_u8(a), dev_scales(a_s, layout), dev_u8(b), dev_f32(b_s))
     torch.cuda.synchronize()
     return host_bits16(c)
 
 
-def test_tiny():
+@pytest.mark.parametrize("layout", ["kb", "row"])
+def test_tiny(layout):
     a, a_s, b, b_s = operands(16, 256, 512, I.TINY)
-    check_gemm_full(run(a, a_s, b, b_s), a, a_s, b, b_s, "tiny")
+    check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, "tiny")
 
 
-def test_decode_qa():
+@pytest.mark.parametrize("layout", ["kb", "row"])
+def test_decode_qa(layout):
     a, a_s, b, b_s = operands(32, 1536, 7168, I.DECODE_QA, outliers=0.01)
-    check_gemm_full(run(a, a_s, b, b_s), a, a_s, b, b_s, "decode_qa")
+    check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, "decode_qa")
 
 
-def test_ragged_ue8m0():
+@pytest.mark.parametrize("layout", ["kb", "row"])
+def test_ragged_ue8m0(layout):
     a, a_s, b, b_s = operands(333, 2500, 1000, I.RAGGED, ue8m0=True)
-    check_gemm_full(run(a, a_s, b, b_s), a, a_s, b, b_s, "ragged")
+    check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, "ragged")
 
 
+@pytest.mark.parametrize("layout", ["kb", "row"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (1, 256, 128), (129, 130, 300), (200, 64, 200), (65, 300, 100),
-                                   (17, 129, 99), (128, 128, 256), (300, 520, 1544), (2, 2000, 16)])
-def test_edge_shapes(M, N, K):
+                                   (17, 129, 99), (128, 128, 256), (300, 520, 1544), (2, 2000, 16),
+                                   (257, 384, 640), (100, 1000, 4096)])
+def test_edge_shapes(M, N, K, layout):
     a, a_s, b, b_s = operands(M, N, K, I.TINY)
-    check_gemm_full(run(a, a_s, b, b_s), a, a_s, b, b_s, f"{M}x{N}x{K}")
+    check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, f"{M}x{N}x{K}")
+
+
+def test_layouts_bit_identical():
+    # The storage order of the activation scales changes only how they are
+    # fetched, never the arithmetic.
+    a, a_s, b, b_s = operands(300, 520, 1536, I.TINY)
+    assert np.array_equal(run(a, a_s, b, b_s, "kb"), run(a, a_s, b, b_s, "row"))
 
 
 def test_k_zero_writes_zeros():
@@ -100,10 +112,11 @@ def test_one_hot_weight():
 
 
 def test_strided_operands():
-    a, a_s, b, b_s = operands(100, 200, 384, I.TINY)
-    A = np.zeros((100, 512), np.uint8); A[:, :384] = a
+    a, a_s, b, b_s = operands(200, 200, 384, I.TINY)
+    A = np.zeros((200, 512), np.uint8); A[:, :384] = a
     B = np.zeros((200, 400), np.uint8); B[:, 16:400] = b
-    c = ds.gemm(dev_u8(A)[:, :384], dev_f32(a_s), dev_u8(B)[:, 16:400], dev_f32(b_s))
+    S = np.zeros((200, 5), np.float32); S[:, 1:4] = a_s           # row stride 5
+    c = ds.gemm(dev_u8(A)[:, :384], dev_f32(S)[:, 1:4], dev_u8(B)[:, 16:400], dev_f32(b_s))
     torch.cuda.synchronize()
     check_gemm_full(host_bits16(c), a, a_s, b, b_s, "strided")
 

@@ -17,7 +17,7 @@ from block_scaled_fp8_act_amd import inputs as I
 from oracle import gemm as G
 from oracle import quant as Q
 
-from gpu_helpers import check_product, dev_f32, dev_u8, host_bits16, host_u8
+from gpu_helpers import check_product, dev_f32, dev_scales, dev_u8, host_bits16, host_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,8 @@ def _case(counts, N, K, seed):
     return a, a_s, b, b_s, off
 
 
-def _run(a, a_s, b, b_s, off):
-    c = ds.grouped_gemm(dev_u8(a), dev_f32(a_s), dev_u8(b), dev_f32(b_s), torch.from_numpy(off).cuda())
+def _run(a, a_s, b, b_s, off, layout="kb"):
+    c = ds.grouped_gemm(dev_u8(a), dev_scales(a_s, layout), dev_u8(b), dev_f32(b_s), torch.from_numpy(off).cuda())
     torch.cuda.synchronize()
     return host_bits16(c)
 
@@ -58,16 +58,17 @@ def _check_all(C, a, a_s, b, b_s, off, what):
     ([0, 0, 129, 0], 64, 1000),
     ([130, 127, 128, 1, 255], 384, 256),
 ])
-def test_grouped_small(counts, N, K):
+@pytest.mark.parametrize("layout", ["kb", "row"])
+def test_grouped_small(counts, N, K, layout):
     a, a_s, b, b_s, off = _case(counts, N, K, len(counts))
-    C = _run(a, a_s, b, b_s, off)
+    C = _run(a, a_s, b, b_s, off, layout)
     _check_all(C, a, a_s, b, b_s, off, f"{counts}")
 
 
 def test_single_expert_equals_dense():
     a, a_s, b, b_s, off = _case([333], 2500, 1000, 3)
     C = _run(a, a_s, b, b_s, off)
-    Cd = ds.gemm(dev_u8(a), dev_f32(a_s), dev_u8(b[0]), dev_f32(b_s[0]))
+    Cd = ds.gemm(dev_u8(a), dev_scales(a_s, "kb"), dev_u8(b[0]), dev_f32(b_s[0]))
     torch.cuda.synchronize()
     assert np.array_equal(C, host_bits16(Cd))
 
