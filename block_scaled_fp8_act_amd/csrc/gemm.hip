@@ -30,7 +30,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;
 constexpr int kXcds = 8;
-constexpr int kGroupM = 8;
+#ifndef DSFP8_GROUP_M
+#define DSFP8_GROUP_M 8
+#endif
+constexpr int kGroupM = DSFP8_GROUP_M;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct Cfg {
@@ -149,7 +152,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, 
     const uint16_t* src = cst + r * CS + cc * 8;
     uint16_t* dst = p.C + row * p.ldc + col;
     if (cvec && col + 8 <= N) {
+#ifdef DSFP8_NT_STORE
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst));
+#else
       *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+#endif
     } else {
       for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = src[e];
     }
@@ -327,10 +334,14 @@ struct DmaCfg {
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
 };
 
+// Large products: 256x256 tiles, 8 waves of 128x64 (one workgroup per CU);
+// small or skinny products and the grouped form: 128x128 tiles, 4 waves of
+// 64x64 (two workgroups per CU).
 #ifndef DSFP8_DMA_TILE
-#define DSFP8_DMA_TILE 128, 128, 2, 2, 2
+#define DSFP8_DMA_TILE 256, 256, 2, 4, 2
 #endif
-using CfgDma = DmaCfg<DSFP8_DMA_TILE>;
+using CfgDmaBig = DmaCfg<DSFP8_DMA_TILE>;
+using CfgDma = DmaCfg<128, 128, 2, 2, 2>;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -447,17 +458,30 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
     v8i bfr[CF::TN];
 #pragma unroll
     for (int j = 0; j < CF::TN; ++j) bfr[j] = read_frag(bt, wn * CF::WN + j * 16 + fr, fg);
+    // Row-subtile i's MFMAs are issued before the rescale of row-subtile
+    // i-1, so the fma of a partial product never waits for the MFMA that has
+    // just produced it.
+    v4f part[2][CF::TN];
+    v4f scv[2];
 #pragma unroll
-    for (int i = 0; i < CF::TM; ++i) {
-      const v8i afr = read_frag(at, wm * CF::WM + i * 16 + fr, fg);
-      const int srow4 = wm * CF::WM + i * 16 + 4 * fg;  // first of this lane's 4 rows
-      const v4f sc = *reinterpret_cast<const v4f*>(sarea + (srow4 / CF::SA_ROWS) * CF::SAW + srow4 % CF::SA_ROWS) * bsv;
+    for (int i = 0; i <= CF::TM; ++i) {
+      if (i < CF::TM) {
+        const v8i afr = read_frag(at, wm * CF::WM + i * 16 + fr, fg);
+        const int srow4 = wm * CF::WM + i * 16 + 4 * fg;  // first of this lane's 4 rows
+        scv[i & 1] =
+            *reinterpret_cast<const v4f*>(sarea + (srow4 / CF::SA_ROWS) * CF::SAW + srow4 % CF::SA_ROWS) * bsv;
 #pragma unroll
-      for (int j = 0; j < CF::TN; ++j) {
-        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+        for (int j = 0; j < CF::TN; ++j)
+          part[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+      }
+      if (i > 0) {
+        const int r = i - 1;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc[v], acc[i][j][v]);
+        for (int j = 0; j < CF::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[r][j][v] = __builtin_fmaf(part[r & 1][j][v], scv[r & 1][v], acc[r][j][v]);
       }
     }
   }
@@ -469,9 +493,11 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 // GROUP_M-row groups inside a range.
 __device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
   const int64_t total = tiles_m * tiles_n;
+#ifndef DSFP8_NO_XCD_REMAP
   const int64_t q = total / kXcds, r = total % kXcds;
   const int64_t xcd = pid % kXcds, idx = pid / kXcds;
   pid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+#endif
   const int64_t per_group = (int64_t)kGroupM * tiles_n;
   const int64_t gid = pid / per_group;
   const int64_t first_m = gid * kGroupM;
@@ -638,6 +664,11 @@ dim3 grouped_grid(const GemmArgs& a) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
+  if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) == 0) {
+    hipLaunchKernelGGL((gemm_kernel<CfgDmaBig, 0>), dense_grid<CfgDmaBig>(a), dim3(CfgDmaBig::kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);
 }
 

@@ -63,6 +63,14 @@ def test_edge_shapes(M, N, K, layout):
     check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("layout", ["kb", "row"])
+def test_large_tile_path_with_tails(layout):
+    # Enough 256x256 tiles to select the large-tile pipeline, with partial
+    # tiles in M (1300 = 5*256 + 20) and N (11000 = 42*256 + 248); full check.
+    a, a_s, b, b_s = operands(1300, 11000, 640, I.TINY)
+    check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, "1300x11000x640")
+
+
 def test_layouts_bit_identical():
     # The storage order of the activation scales changes only how they are
     # fetched, never the arithmetic.
