@@ -310,6 +310,34 @@ def recorded_traffic():
 
 # ---- main --------------------------------------------------------------------------------------
 
+def only(kernel, reps, dev):
+    """Run one kernel of the dense step `reps` times (for counter collection)."""
+    if kernel == "copy":
+        # calibration: a plain 1 GiB device-to-device copy (1 GiB read, 1 GiB written)
+        src = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            dst.copy_(src)
+    else:
+        st = setup_dense(dev)
+        T = Timer()
+        b, F = st["b"], st["F"]
+        fns = {
+            "act_quant": lambda: ds.act_quant(b["x"], out=(b["xq"], b["xs"])),
+            "gemm_up": lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"]),
+            "silu_mul_act_quant": lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:],
+                                                                out=(b["hq"], b["hs"])),
+            "gemm_down": lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"]),
+        }
+        dense_step(st, T)  # produce valid inputs for every stage
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            fns[kernel]()
+    torch.cuda.synchronize()
+    print(json.dumps({"only": kernel, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +345,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["act_quant", "gemm_up", "silu_mul_act_quant", "gemm_down", "copy"],
+                    help="run one kernel of the dense step --reps times and exit (for rocprofv3 counters)")
+    ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -328,6 +359,9 @@ def main():
         sys.exit(2)
     ds._lib.load()
     dev = torch.device("cuda:0")
+    if args.only:
+        only(args.only, args.reps, dev)
+        return
     props = torch.cuda.get_device_properties(dev)
 
     st = setup_dense(dev)

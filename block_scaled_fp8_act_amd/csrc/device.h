@@ -72,6 +72,29 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   return __builtin_fmaf(-t, r, q);
 }
 
+// ---- division by a launch constant ------------------------------------------------
+
+// n / d for 0 <= n < 2^31 by multiply and shift (Granlund and Montgomery's
+// round-up method with N = 31): with l = ceil(log2 d) and
+// m = floor(2^(31+l) / d) + 1 < 2^32, n / d == (n * m) >> (31 + l).
+struct FastDiv {
+  uint32_t d, m, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while (((uint64_t)1 << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.m = (uint32_t)((((uint64_t)1) << (31 + l)) / d + 1);
+  f.shift = 31 + l;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.shift);
+}
+
 // ---- cross-lane reductions -------------------------------------------------------
 
 template <int CTRL>

@@ -29,11 +29,6 @@ __device__ __forceinline__ u32x4 mk4(uint32_t a, uint32_t b, uint32_t c, uint32_
   return v;
 }
 
-struct Unit {
-  int64_t m;
-  int64_t b;
-};
-
 // Activation quantisation of one (row, block) unit held by 16 lanes.
 // `v` holds this lane's 8 values (already SiLU-gated if fused); `valid` says
 // which of them are real columns.  Writes y, s (and nothing for padding).
@@ -108,36 +103,39 @@ __device__ __forceinline__ float silu_mul_bf16(float g, float u, __bf16* hb) {
   return (float)(*hb);
 }
 
+// A wave-unit is (row group g, K-block b): DPP row r of the wave (lanes
+// 16r..16r+15) quantises row 4g + r of block b.  Wave-units are numbered
+// block-major (w = b * G + g), so consecutive waves read consecutive row
+// groups of the same column block and their scale stores (four consecutive
+// rows, one K-block) are contiguous when the scales are stored K-block-major.
 template <bool VEC, bool FUSED>
-__global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int64_t nb, int64_t step_m,
-                                                             int64_t step_b) {
-  const int lane16 = threadIdx.x & 15;
-  const int64_t group = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;
-  Unit u;
-  u.m = group / nb;
-  u.b = group - u.m * nb;
-  while (u.m < a.M) {
-    Unit us[kUnroll];
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int64_t nb, FastDiv G, bool fast) {
+  const int lane = threadIdx.x & 63;
+  const int lane16 = lane & 15;
+  const int drow = lane >> 4;
+  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t wave0 = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t total = (int64_t)G.d * nb;
+  for (int64_t base = wave0; base < total; base += waves * kUnroll) {
     u32x4 wg[kUnroll], wu[kUnroll];
+    int64_t ms[kUnroll], bs[kUnroll];
+    bool live[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      us[i] = u;
-      const bool live = u.m < a.M;
-      const int64_t col = u.b * kBlock + lane16 * 8;
-      wg[i] = load8<VEC>(a.g, a.ldg, u.m, col, a.K, live);
-      if (FUSED) wu[i] = load8<VEC>(a.u, a.ldu, u.m, col, a.K, live);
-      u.b += step_b;
-      u.m += step_m;
-      if (u.b >= nb) {
-        u.b -= nb;
-        u.m += 1;
-      }
+      const int64_t w = base + i * waves;
+      const int64_t b = fast ? (int64_t)fastdiv((uint32_t)w, G) : w / (int64_t)G.d;
+      const int64_t m = (w - b * (int64_t)G.d) * 4 + drow;
+      live[i] = w < total && m < a.M;
+      ms[i] = m;
+      bs[i] = b;
+      const int64_t col = b * kBlock + lane16 * 8;
+      wg[i] = load8<VEC>(a.g, a.ldg, m, col, a.K, live[i]);
+      if (FUSED) wu[i] = load8<VEC>(a.u, a.ldu, m, col, a.K, live[i]);
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const bool live = us[i].m < a.M;
-      const int64_t col = us[i].b * kBlock + lane16 * 8;
-      int64_t rem = a.K - col;
+      const int64_t col = bs[i] * kBlock + lane16 * 8;
+      const int64_t rem = a.K - col;
       const int nvalid = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
       float v[8];
       unpack8(wg[i], v);
@@ -147,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int
         __bf16 hb[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = silu_mul_bf16(v[j], uv[j], &hb[j]);
-        if (a.h != nullptr && live) {
-          uint16_t* hrow = a.h + us[i].m * a.ldh + col;
+        if (a.h != nullptr && live[i]) {
+          uint16_t* hrow = a.h + ms[i] * a.ldh + col;
           if (VEC) {
             if (nvalid == 8) {
               u32x4 o;
@@ -165,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int
           }
         }
       }
-      quantise_unit<VEC>(v, nvalid, a, us[i].m, us[i].b, lane16, live);
+      quantise_unit<VEC>(v, nvalid, a, ms[i], bs[i], lane16, live[i]);
     }
   }
 }
@@ -236,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void weight_quant_kernel(WeightQuantArgs 
 // v_cvt_pk_bf16_f32 and stores 32 bytes.  A workgroup covers 4096 columns of
 // kDqRows rows.
 
-constexpr int kDqRows = 4;
+constexpr int kDqRows = 8;
 
 __device__ __forceinline__ void dequant16(const u32x4 w, float s, u32x4& o0, u32x4& o1) {
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -259,29 +257,40 @@ __global__ __launch_bounds__(kThreads) void weight_dequant_kernel(DequantArgs a)
   if (col >= a.K) return;
   const int64_t row0 = (int64_t)blockIdx.y * kDqRows;
   const int64_t kb = col / kBlock;
+  // All rows' loads are issued before any conversion, so kDqRows 16-byte
+  // loads per lane are in flight at once.
+  u32x4 w[kDqRows];
+  float sc[kDqRows];
 #pragma unroll
   for (int r = 0; r < kDqRows; ++r) {
     const int64_t n = row0 + r;
-    if (n >= a.N) return;
-    const float s = a.S[(n / kBlock) * a.ldS + kb];
-    const uint8_t* src = a.w + n * a.ldw + col;
-    uint16_t* dst = a.out + n * a.ldo + col;
+    const bool ok = n < a.N;
+    const int64_t nn = ok ? n : row0;
+    sc[r] = a.S[(nn / kBlock) * a.ldS + kb];
+    const uint8_t* src = a.w + nn * a.ldw + col;
     if (VEC) {
-      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-      u32x4 o0, o1;
-      dequant16(w, s, o0, o1);
-      __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(dst));
-      __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(dst) + 1);
+      w[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     } else {
       uint32_t bytes[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) bytes[j] = (col + j < a.K) ? src[j] : 0u;
-      u32x4 w = mk4(bytes[0] | bytes[1] << 8 | bytes[2] << 16 | bytes[3] << 24,
-                           bytes[4] | bytes[5] << 8 | bytes[6] << 16 | bytes[7] << 24,
-                           bytes[8] | bytes[9] << 8 | bytes[10] << 16 | bytes[11] << 24,
-                           bytes[12] | bytes[13] << 8 | bytes[14] << 16 | bytes[15] << 24);
-      u32x4 o0, o1;
-      dequant16(w, s, o0, o1);
+      w[r] = mk4(bytes[0] | bytes[1] << 8 | bytes[2] << 16 | bytes[3] << 24,
+                 bytes[4] | bytes[5] << 8 | bytes[6] << 16 | bytes[7] << 24,
+                 bytes[8] | bytes[9] << 8 | bytes[10] << 16 | bytes[11] << 24,
+                 bytes[12] | bytes[13] << 8 | bytes[14] << 16 | bytes[15] << 24);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kDqRows; ++r) {
+    const int64_t n = row0 + r;
+    if (n >= a.N) break;
+    u32x4 o0, o1;
+    dequant16(w[r], sc[r], o0, o1);
+    uint16_t* dst = a.out + n * a.ldo + col;
+    if (VEC) {
+      __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(dst) + 1);
+    } else {
       const uint32_t outw[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -297,25 +306,27 @@ inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_
 hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.K == 0) return hipSuccess;
   const int64_t nb = (a.K + kBlock - 1) / kBlock;
-  const int64_t units = a.M * nb;
+  const int64_t G = (a.M + 3) / 4;  // groups of four rows
+  const FastDiv gdiv = make_fastdiv((uint32_t)G);
   const bool fused = a.u != nullptr;
   // 16-byte loads of x (and u), 8-byte stores of y, 16-byte stores of h.
   bool vec = (a.K % 8 == 0) && aligned(a.g, 16) && (a.ldg % 8 == 0) && aligned(a.y, 8) && (a.ldy % 8 == 0);
   if (fused) vec = vec && aligned(a.u, 16) && (a.ldu % 8 == 0);
   if (a.h) vec = vec && aligned(a.h, 16) && (a.ldh % 8 == 0);
-  const int64_t groups_per_wg = kThreads / 16;
-  const int64_t want = (units + groups_per_wg * kUnroll - 1) / (groups_per_wg * kUnroll);
+  const int64_t waves_per_wg = kThreads / 64;
+  const int64_t want = (G * nb + waves_per_wg * kUnroll - 1) / (waves_per_wg * kUnroll);
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int64_t grid = want < cap ? want : cap;
-  const int64_t G = grid * groups_per_wg;
-  const int64_t step_m = G / nb, step_b = G % nb;
+  // The multiply-shift division needs every wave-unit index the loop forms
+  // (up to kUnroll grid-widths past the end) below 2^31.
+  const bool fast = G * nb + (int64_t)kUnroll * grid * waves_per_wg < ((int64_t)1 << 31);
   dim3 g((unsigned)grid), blk(kThreads);
   if (fused) {
-    if (vec) hipLaunchKernelGGL((act_quant_kernel<true, true>), g, blk, 0, stream, a, nb, step_m, step_b);
-    else hipLaunchKernelGGL((act_quant_kernel<false, true>), g, blk, 0, stream, a, nb, step_m, step_b);
+    if (vec) hipLaunchKernelGGL((act_quant_kernel<true, true>), g, blk, 0, stream, a, nb, gdiv, fast);
+    else hipLaunchKernelGGL((act_quant_kernel<false, true>), g, blk, 0, stream, a, nb, gdiv, fast);
   } else {
-    if (vec) hipLaunchKernelGGL((act_quant_kernel<true, false>), g, blk, 0, stream, a, nb, step_m, step_b);
-    else hipLaunchKernelGGL((act_quant_kernel<false, false>), g, blk, 0, stream, a, nb, step_m, step_b);
+    if (vec) hipLaunchKernelGGL((act_quant_kernel<true, false>), g, blk, 0, stream, a, nb, gdiv, fast);
+    else hipLaunchKernelGGL((act_quant_kernel<false, false>), g, blk, 0, stream, a, nb, gdiv, fast);
   }
   return hipGetLastError();
 }
