@@ -223,17 +223,25 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
     xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
     xs = ds.new_scales(M, kb(K), dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    T = Timer()
     for i in range(copies + 3):
         ds.act_quant(x, fmt, out=(xq, xs))
         ds.gemm(xq, xs, *ws[i % copies], out=out)
     torch.cuda.synchronize()
-    for i in range(iters):
-        T.run("act_quant", lambda: ds.act_quant(x, fmt, out=(xq, xs)))
-        q, s = ws[i % copies]
-        T.run("gemm", lambda: ds.gemm(xq, xs, q, s, out=out))
-    T.collect()
-    g_us, a_us = T.avg_us("gemm"), T.avg_us("act_quant")
+
+    # Kernels this short are timed as back-to-back launches between one event
+    # pair (an event pair around each launch adds a fixed floor of several us).
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    a_us = timed(lambda i: ds.act_quant(x, fmt, out=(xq, xs)))
+    g_us = timed(lambda i: ds.gemm(xq, xs, *ws[i % copies], out=out))
     fl, by = 2.0 * M * N * K, gemm_bytes(M, N, K)
     roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
     return {"workload": name, "gemm": {"us": round(g_us, 2), "tflops": round(fl / g_us / 1e6, 2),

@@ -192,10 +192,8 @@ dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t l
 }
 
 size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return 0;
+  return dsfp8::gemm_workspace_bytes(M, N, K);
 }
 
 dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
@@ -207,8 +205,10 @@ dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as
   DSFP8_TRY(check_mat(B, N, K, ldb, 1));
   DSFP8_TRY(check_mat(b_s, nblk(N), nblk(K), ldbs, 4));
   DSFP8_TRY(check_mat(C, M, N, ldc, 2));
-  if (workspace_bytes < dsfp8_gemm_workspace_bytes(M, N, K)) return DSFP8_ERR_WORKSPACE;
-  (void)workspace;
+  const size_t need = dsfp8_gemm_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
+  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
+  if (!al(workspace, 16)) return DSFP8_ERR_ALIGN;
   dsfp8::GemmArgs a{};
   a.A = static_cast<const uint8_t*>(A);
   a.lda = lda;
@@ -224,6 +224,7 @@ dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as
   a.M = M;
   a.N = N;
   a.K = K;
+  a.partial = static_cast<float*>(workspace);
   return launched(dsfp8::launch_gemm(a, stream));
 }
 

@@ -116,6 +116,8 @@ struct TileRef {
   const float* b_s;      // this tile's weight scales
   int64_t row0, row_end; // rows [row0, min(row0 + BM, row_end)) are computed
   int64_t n0;
+  int kb0, kb1;          // K-blocks [kb0, kb1) are accumulated
+  float* partial;        // non-null: store the fp32 partial [M, N] here instead of C
 };
 
 // Epilogue: round to bf16, stage each wave's WM x WN tile in LDS (which the
@@ -161,6 +163,24 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, 
       for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = src[e];
     }
   }
+}
+
+// Split K: the fp32 partial of this tile goes straight from registers to the
+// workspace [M, N] of its split (16 lanes write 64 contiguous bytes).
+template <class CF>
+__device__ __forceinline__ void store_partial(const GemmArgs& p, const TileRef& t,
+                                              const v4f (&acc)[CF::TM][CF::TN], int wm, int wn, int lane) {
+  const int fr = lane & 15, fg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < CF::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = t.row0 + wm * CF::WM + i * 16 + 4 * fg + v;
+        const int64_t col = t.n0 + wn * CF::WN + j * 16 + fr;
+        if (row < t.row_end && col < p.N) t.partial[row * p.N + col] = acc[i][j][v];
+      }
 }
 
 template <class CF, int VEC>
@@ -225,16 +245,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
   if (nbi > kbn - 1) nbi = kbn - 1;
   const float* bsrow = t.b_s + nbi * p.ldbs;
 
-  if (nkb > 0) {
-    gload(0);
+  const int kb0 = t.kb0, kb1 = t.kb1;
+  (void)nkb;
+  if (kb0 < kb1) {
+    gload(kb0);
     lstore(0);
   }
   __syncthreads();
 
   const int fr = lane & 15, fg = lane >> 4;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int buf = (kb - kb0) & 1;
+    if (kb + 1 < kb1) gload(kb + 1);
     const float bsv = bsrow[kb];
     const uint8_t* at = As + buf * CF::A_BYTES;
     const uint8_t* bt = Bs + buf * CF::B_BYTES;
@@ -254,11 +276,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
         for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc[v], acc[i][j][v]);
       }
     }
-    if (kb + 1 < nkb) lstore(buf ^ 1);
+    if (kb + 1 < kb1) lstore(buf ^ 1);
     __syncthreads();
   }
 
   __syncthreads();
+  if (t.partial != nullptr) {
+    store_partial<CF>(p, t, acc, wm, wn, lane);
+    return;
+  }
   store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
 }
 
@@ -440,17 +466,19 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 #pragma unroll
     for (int j = 0; j < CF::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+  const int kb0 = t.kb0, kb1 = t.kb1;
+  (void)nkb;
 #pragma unroll
   for (int s = 0; s < CF::STAGES - 1; ++s)
-    if (s < nkb) issue(s, s);
+    if (kb0 + s < kb1) issue(kb0 + s, s);
 
   const int fr = lane & 15, fg = lane >> 4;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int later = (nkb - 1 - kb) < (CF::STAGES - 2) ? (nkb - 1 - kb) : (CF::STAGES - 2);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int later = (kb1 - 1 - kb) < (CF::STAGES - 2) ? (kb1 - 1 - kb) : (CF::STAGES - 2);
     wait_stage<CF>(later);
     __syncthreads();
-    if (kb + CF::STAGES - 1 < nkb) issue(kb + CF::STAGES - 1, (kb + CF::STAGES - 1) % CF::STAGES);
-    const uint8_t* st = smem + (kb % CF::STAGES) * CF::STAGE_BYTES;
+    if (kb + CF::STAGES - 1 < kb1) issue(kb + CF::STAGES - 1, (kb - kb0 + CF::STAGES - 1) % CF::STAGES);
+    const uint8_t* st = smem + ((kb - kb0) % CF::STAGES) * CF::STAGE_BYTES;
     const float* sarea = reinterpret_cast<const float*>(st + CF::S_OFF);
     const float bsv = sarea[wave * CF::SAW + CF::SA_ROWS];
     const uint8_t* at = st;
@@ -486,6 +514,10 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
     }
   }
   __syncthreads();
+  if (t.partial != nullptr) {
+    store_partial<CF>(p, t, acc, wm, wn, lane);
+    return;
+  }
   store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
 }
 
@@ -530,7 +562,62 @@ __global__ __launch_bounds__(CF::kThreads) void gemm_kernel(GemmArgs p) {
   t.row0 = tm * CF::BM;
   t.row_end = p.M;
   t.n0 = tn * CF::BN;
+  t.kb0 = 0;
+  t.kb1 = (int)((p.K + BK - 1) / BK);
+  t.partial = nullptr;
+  if (gridDim.y > 1) {
+    // split K: blockIdx.y selects a contiguous range of K-blocks
+    const int per = (t.kb1 + (int)gridDim.y - 1) / (int)gridDim.y;
+    t.kb0 = (int)blockIdx.y * per;
+    t.kb1 = t.kb0 + per < t.kb1 ? t.kb0 + per : t.kb1;
+    t.partial = p.partial + (int64_t)blockIdx.y * p.M * p.N;
+  }
   run_tile<CF, VEC>(p, t, smem);
+}
+
+// Sum the split-K partials in split order (deterministic) and round to bf16.
+// Each thread owns four consecutive outputs and keeps eight splits' loads in
+// flight before adding them in order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int splits) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t MN = p.M * p.N;
+  if (i >= MN) return;
+  const bool full = i + 4 <= MN && (MN & 3) == 0;
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < splits; k0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (k0 + u < splits) {
+        const float* src = p.partial + (int64_t)(k0 + u) * MN + i;
+        if (full) {
+          v[u] = *reinterpret_cast<const float4*>(src);
+        } else {
+          v[u].x = src[0];
+          if (i + 1 < MN) v[u].y = src[1];
+          if (i + 2 < MN) v[u].z = src[2];
+          if (i + 3 < MN) v[u].w = src[3];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (k0 + u < splits) {
+        s[0] += v[u].x;
+        s[1] += v[u].y;
+        s[2] += v[u].z;
+        s[3] += v[u].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t idx = i + e;
+    if (idx >= MN) break;
+    const int64_t row = idx / p.N, col = idx - row * p.N;
+    p.C[row * p.ldc + col] = __builtin_bit_cast(uint16_t, (__bf16)s[e]);
+  }
 }
 
 // Expert row range [lo, hi) with every bound clamped into [0, M_total].
@@ -601,6 +688,9 @@ __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) 
   t.row0 = r0 + (slot - ts[e]) * CF::BM;
   t.row_end = r1;
   t.n0 = (int64_t)blockIdx.y * CF::BN;
+  t.kb0 = 0;
+  t.kb1 = (int)((p.K + BK - 1) / BK);
+  t.partial = nullptr;
   run_tile<CF, VEC>(p, t, smem);
 }
 
@@ -662,8 +752,36 @@ dim3 grouped_grid(const GemmArgs& a) {
 
 }  // namespace
 
+int gemm_k_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t nkb = (K + BK - 1) / BK;
+  const int64_t tiles = ((M + CfgDma::BM - 1) / CfgDma::BM) * ((N + CfgDma::BN - 1) / CfgDma::BN);
+  constexpr int64_t kTargetWorkgroups = 512;  // two per CU on a 256-CU part
+  if (M == 0 || N == 0 || nkb < 4 || tiles * 4 >= kTargetWorkgroups) return 1;
+  int64_t splits = (kTargetWorkgroups + tiles - 1) / tiles;
+  if (splits > nkb / 2) splits = nkb / 2;  // at least two K-blocks per split
+  if (splits < 2) return 1;
+  const int64_t per = (nkb + splits - 1) / splits;
+  return (int)((nkb + per - 1) / per);     // no empty split
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = gemm_k_splits(M, N, K);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  const int splits = gemm_k_splits(a.M, a.N, a.K);
+  if (splits > 1 && a.partial != nullptr) {
+    static_assert(CfgDma::BM == Cfg128::BM && CfgDma::BN == Cfg128::BN, "same split grid for both pipelines");
+    dim3 g = dense_grid<CfgDma>(a);
+    g.y = (unsigned)splits;
+    hipError_t err = dispatch<CfgDma, Cfg128, false>(a, g, g, stream);
+    if (err != hipSuccess) return err;
+    const int64_t groups = (a.M * a.N + 1023) / 1024;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
+    return hipGetLastError();
+  }
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) == 0) {
     hipLaunchKernelGGL((gemm_kernel<CfgDmaBig, 0>), dense_grid<CfgDmaBig>(a), dim3(CfgDmaBig::kThreads), 0, stream, a);

@@ -59,6 +59,8 @@ struct GemmArgs {
   const int32_t* offsets;
   int64_t E;
   int32_t* tile_start;  // workspace: E+1 ints
+  // dense form with split K: fp32 partial products [splits, M, N] (workspace)
+  float* partial;
 };
 
 hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream);
@@ -68,6 +70,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 
 size_t grouped_workspace_bytes(int64_t E);
+
+// Number of K splits the dense product uses for this shape (1 = none), and the
+// fp32 workspace that requires.  Small products (few output tiles) split their
+// K-blocks over several workgroups so that the weight streams from every CU.
+int gemm_k_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
