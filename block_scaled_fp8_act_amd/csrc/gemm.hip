@@ -368,6 +368,12 @@ struct DmaCfg {
 #endif
 using CfgDmaBig = DmaCfg<DSFP8_DMA_TILE>;
 using CfgDma = DmaCfg<128, 128, 2, 2, 2>;
+// Grouped form: 64-row tiles (the routed rows of most experts fill less than
+// one), 4 waves of 64x32.
+#ifndef DSFP8_GROUPED_TILE
+#define DSFP8_GROUPED_TILE 64, 128, 1, 4, 2
+#endif
+using CfgGrp = DmaCfg<DSFP8_GROUPED_TILE>;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -521,15 +527,22 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
 }
 
-// Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges, then
-// GROUP_M-row groups inside a range.
-__device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  const int64_t total = tiles_m * tiles_n;
+// Workgroup i runs on XCD i % 8.  Renumber ids 0..total-1 so that each XCD
+// owns one contiguous range (and so shares its L2 among neighbouring tiles).
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t pid, int64_t total) {
 #ifndef DSFP8_NO_XCD_REMAP
   const int64_t q = total / kXcds, r = total % kXcds;
   const int64_t xcd = pid % kXcds, idx = pid / kXcds;
   pid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 #endif
+  return pid;
+}
+
+// Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges, then
+// GROUP_M-row groups inside a range.
+__device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  const int64_t total = tiles_m * tiles_n;
+  pid = xcd_contiguous(pid, total);
   const int64_t per_group = (int64_t)kGroupM * tiles_n;
   const int64_t gid = pid / per_group;
   const int64_t first_m = gid * kGroupM;
@@ -629,46 +642,70 @@ __device__ __forceinline__ void expert_rows(const int32_t* offsets, int64_t e, i
   hi = b;
 }
 
-// tile_start[e] = number of BM-row tiles of experts 0..e-1 (one workgroup).
-__global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* offsets, int64_t E, int64_t M, int bm,
-                                                             int32_t* tile_start) {
+// Tile schedules for up to kMaxClasses row-tile heights: for class c,
+// tile_start[c * (E + 1) + e] = number of bm[c]-row tiles of the experts before
+// e whose row count lies in (lo[c], hi[c]].  One workgroup.
+constexpr int kMaxClasses = 3;
+struct ScheduleClasses {
+  int n;
+  int bm[kMaxClasses];
+  int64_t lo[kMaxClasses], hi[kMaxClasses];
+};
+
+__global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* offsets, int64_t E, int64_t M,
+                                                             ScheduleClasses cls, int32_t* tile_start) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry;
   const int t = threadIdx.x;
-  if (t == 0) {
-    carry = 0;
-    tile_start[0] = 0;
-  }
-  __syncthreads();
-  for (int64_t base = 0; base < E; base += 1024) {
-    const int64_t e = base + t;
-    int32_t cnt = 0;
-    if (e < E) {
-      int64_t lo, hi;
-      expert_rows(offsets, e, M, lo, hi);
-      cnt = (int32_t)((hi - lo + bm - 1) / bm);
+  for (int c = 0; c < cls.n; ++c) {
+    int32_t* ts = tile_start + (int64_t)c * (E + 1);
+    if (t == 0) {
+      carry = 0;
+      ts[0] = 0;
     }
-    part[t] = cnt;
     __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const int32_t add = t >= d ? part[t - d] : 0;
+    for (int64_t base = 0; base < E; base += 1024) {
+      const int64_t e = base + t;
+      int32_t cnt = 0;
+      if (e < E) {
+        int64_t lo, hi;
+        expert_rows(offsets, e, M, lo, hi);
+        const int64_t rows = hi - lo;
+        if (rows > cls.lo[c] && rows <= cls.hi[c]) cnt = (int32_t)((rows + cls.bm[c] - 1) / cls.bm[c]);
+      }
+      part[t] = cnt;
       __syncthreads();
-      part[t] += add;
+      for (int d = 1; d < 1024; d <<= 1) {
+        const int32_t add = t >= d ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += add;
+        __syncthreads();
+      }
+      if (e < E) ts[e + 1] = carry + part[t];
+      __syncthreads();
+      if (t == 1023) carry += part[1023];
       __syncthreads();
     }
-    if (e < E) tile_start[e + 1] = carry + part[t];
-    __syncthreads();
-    if (t == 1023) carry += part[1023];
-    __syncthreads();
   }
 }
 
+// One workgroup per (row tile of an expert, 128-column tile).  The grid is
+// sized for the worst case; the real number of row tiles is ts[E].  Ids past
+// the real work exit at once; the rest are renumbered XCD-contiguously over
+// the real work, column tile fastest, so an expert's rows are fetched once per
+// XCD and reused across its column tiles, and consecutive row tiles of a large
+// expert share each weight tile in L2.
 template <class CF, int VEC>
 __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
-  const int64_t slot = blockIdx.x;
   const int32_t* ts = p.tile_start;
-  if (slot >= ts[p.E]) return;
+  const int64_t tiles_n = (p.N + CF::BN - 1) / CF::BN;
+  const int64_t total = (int64_t)ts[p.E] * tiles_n;
+  const int64_t pid = blockIdx.x;
+  if (pid >= total) return;
+  const int64_t L = xcd_contiguous(pid, total);
+  const int64_t slot = L / tiles_n;
+  const int64_t tn = L - slot * tiles_n;
   // Last expert e with ts[e] <= slot; then ts[e+1] > slot.
   int64_t lo = 0, hi = p.E;  // invariant: ts[lo] <= slot < ts[hi]
   while (hi - lo > 1) {
@@ -687,7 +724,7 @@ __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) 
   t.b_s = p.b_s + e * kbn * p.ldbs;
   t.row0 = r0 + (slot - ts[e]) * CF::BM;
   t.row_end = r1;
-  t.n0 = (int64_t)blockIdx.y * CF::BN;
+  t.n0 = tn * CF::BN;
   t.kb0 = 0;
   t.kb1 = (int)((p.K + BK - 1) / BK);
   t.partial = nullptr;
@@ -747,7 +784,8 @@ dim3 dense_grid(const GemmArgs& a) {
 
 template <class CF>
 dim3 grouped_grid(const GemmArgs& a) {
-  return dim3((unsigned)((a.M + CF::BM - 1) / CF::BM + a.E), (unsigned)((a.N + CF::BN - 1) / CF::BN));
+  const int64_t slots = (a.M + CF::BM - 1) / CF::BM + a.E;  // bound on the row tiles
+  return dim3((unsigned)(slots * ((a.N + CF::BN - 1) / CF::BN)));
 }
 
 }  // namespace
@@ -790,18 +828,54 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);
 }
 
+// Grouped launches.  With the direct-to-LDS pipeline the experts are split
+// into three classes by their row count, each run with its own tile height
+// (64 rows: <= 64; 128 rows: 65..128; 256x256 tiles: > 128), so a row tile is
+// never padded by more than its own height and a large expert streams its
+// weight once per 256 rows instead of once per 64.
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.M == 0) return hipSuccess;
-  // The tile schedule depends on the row-tile height of the pipeline used.
-  const int bm = pick_vec<CfgDma>(a) == 0 ? CfgDma::BM : Cfg128::BM;
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.E, a.M, bm, a.tile_start);
+  const bool dma = pick_vec<CfgGrp>(a) == 0 && pick_vec<CfgDmaBig>(a) == 0;
+  ScheduleClasses cls{};
+  if (dma) {
+    cls.n = 3;
+    cls.bm[0] = CfgGrp::BM;    cls.lo[0] = 0;              cls.hi[0] = CfgGrp::BM;
+    cls.bm[1] = CfgDma::BM;    cls.lo[1] = CfgGrp::BM;     cls.hi[1] = CfgDma::BM;
+    cls.bm[2] = CfgDmaBig::BM; cls.lo[2] = CfgDma::BM;     cls.hi[2] = a.M;
+  } else {
+    cls.n = 1;
+    cls.bm[0] = Cfg128::BM;    cls.lo[0] = 0;              cls.hi[0] = a.M;
+  }
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.E, a.M, cls, a.tile_start);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return dispatch<CfgDma, Cfg128, true>(a, grouped_grid<CfgDma>(a), grouped_grid<Cfg128>(a), stream);
+  if (!dma) return dispatch<CfgDma, Cfg128, true>(a, grouped_grid<CfgDma>(a), grouped_grid<Cfg128>(a), stream);
+  const int64_t E = a.E, M = a.M;
+  auto tiles_n = [&](int bn) { return (a.N + bn - 1) / bn; };
+  auto mn = [](int64_t x, int64_t y) { return x < y ? x : y; };
+  // Bounds on each class's row tiles: one per expert for the two small
+  // classes; for the large class at most M/256 + (experts with > 128 rows).
+  GemmArgs c0 = a, c1 = a, c2 = a;
+  c1.tile_start = a.tile_start + (E + 1);
+  c2.tile_start = a.tile_start + 2 * (E + 1);
+  const int64_t s0 = mn(E, M), s1 = mn(E, M / (CfgGrp::BM + 1)), s2 = (M + CfgDmaBig::BM - 1) / CfgDmaBig::BM + mn(E, M / (CfgDma::BM + 1));
+  if (s0 > 0) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<CfgGrp, 0>), dim3((unsigned)(s0 * tiles_n(CfgGrp::BN))),
+                       dim3(CfgGrp::kThreads), 0, stream, c0);
+  }
+  if (s1 > 0) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<CfgDma, 0>), dim3((unsigned)(s1 * tiles_n(CfgDma::BN))),
+                       dim3(CfgDma::kThreads), 0, stream, c1);
+  }
+  if (s2 > 0) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<CfgDmaBig, 0>), dim3((unsigned)(s2 * tiles_n(CfgDmaBig::BN))),
+                       dim3(CfgDmaBig::kThreads), 0, stream, c2);
+  }
+  return hipGetLastError();
 }
 
 size_t grouped_workspace_bytes(int64_t E) {
-  const size_t n = (size_t)(E + 1) * sizeof(int32_t);
+  const size_t n = (size_t)kMaxClasses * (size_t)(E + 1) * sizeof(int32_t);
   return (n + 255) & ~(size_t)255;
 }
 
