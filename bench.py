@@ -253,43 +253,50 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
 
 # ---- CPU baseline ---------------------------------------------------------------------------
 
-def cpu_baseline():
+def cpu_baseline(budget_s=15.0):
     """The CPU oracle on a bounded sample of the dense FFN step.
 
-    Sample: 128 token rows; 1536 rows each of w1 and w3 (3072 outputs of the
-    up-projection) over the full K = 7168; SiLU gate; 1536 rows of w2 over
-    the first 1536 of its K columns.  Weights are drawn and quantised on the
-    host before timing; the timed part is act_quant, the up product, the gate,
-    act_quant of h and the down product, all in the oracle.  Reported as the
-    sample's GEMM flop per second.
+    Sample: chunks of 128 token rows (eight distinct chunks, cycled); 1536
+    rows each of w1 and w3 (3072 outputs of the up-projection) over the full
+    K = 7168; SiLU gate; 1536 rows of w2 over the first 1536 of its K columns.
+    Weights and activations are drawn and quantised on the host before
+    timing; each timed chunk runs act_quant, the up product, the gate,
+    act_quant of h and the down product, all in the oracle.  Chunks run until
+    ``budget_s`` seconds of oracle time have passed.  Reported as the sample's
+    GEMM flop per second.
     """
     import threadpoolctl
     from oracle import gemm as G
     from oracle import glue
     from oracle import quant as Q
+    from oracle.formats import f32_to_bf16
 
-    Ms, D, Fs = 128, 7168, 1536
-    x = I.activations((Ms, D), I.DENSE_FFN, 900)
+    Ms, D, Fs, n_chunks = 128, 7168, 1536, 8
+    xs = [I.activations((Ms, D), I.DENSE_FFN, 900 + c) for c in range(n_chunks)]
     w13 = Q.weight_quant(I.weights_f32((2 * Fs, D), I.DENSE_FFN, 901))
     w2 = Q.weight_quant(I.weights_f32((Fs, Fs), I.DENSE_FFN, 902))
-    from oracle.formats import f32_to_bf16
-    t0 = time.perf_counter()
-    a, a_s = Q.act_quant(x)
-    h13 = f32_to_bf16(G.gemm(a, a_s, *w13))
-    h = glue.silu_mul(h13[:, :Fs], h13[:, Fs:])
-    hq, hs = Q.act_quant(h)
-    _ = G.gemm(hq, hs, *w2)
-    dt = time.perf_counter() - t0
-    flop = 2.0 * Ms * 2 * Fs * D + 2.0 * Ms * Fs * Fs
+    dt, done = 0.0, 0
+    while dt < budget_s:
+        x = xs[done % n_chunks]
+        t0 = time.perf_counter()
+        a, a_s = Q.act_quant(x)
+        h13 = f32_to_bf16(G.gemm(a, a_s, *w13))
+        h = glue.silu_mul(h13[:, :Fs], h13[:, Fs:])
+        hq, hs = Q.act_quant(h)
+        _ = G.gemm(hq, hs, *w2)
+        dt += time.perf_counter() - t0
+        done += 1
+    flop = done * (2.0 * Ms * 2 * Fs * D + 2.0 * Ms * Fs * Fs)
     try:
         blas = threadpoolctl.threadpool_info()
         threads = max([b.get("num_threads", 1) for b in blas] + [1])
     except Exception:
         threads = 1
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "dense FFN step on 128 tokens x (3072 up-projection outputs, K=7168) + SiLU gate + "
-                      "(1536 down outputs, K=1536); fp64 products through NumPy BLAS, quantisers in NumPy"}
+            "kind": "oracle", "seconds": round(dt, 2), "chunks": done,
+            "sample": f"dense FFN step on {done} chunks of 128 tokens x (3072 up-projection outputs, K=7168) "
+                      "+ SiLU gate + (1536 down outputs, K=1536); fp64 products through NumPy BLAS, "
+                      "quantisers in NumPy"}
 
 
 # ---- traffic (from the committed rocprofv3 counter summary) -----------------------------------
