@@ -85,15 +85,16 @@ __device__ __forceinline__ u32x4 load_chunk(const uint8_t* row, int64_t k, int64
   return v;
 }
 
-// Byte offset of 16-byte chunk c of tile row r in LDS.  gfx950's LDS serves
-// 16 lanes x 16 bytes per cycle from 64 four-byte banks, so a 128-byte row
-// covers half of the banks and the row's parity selects the half; XOR-ing the
-// chunk index with (r >> 1) & 7 spreads the 16 rows of an MFMA fragment read
-// over all 64 banks.
-#ifndef DSFP8_SWZ_SHIFT
-#define DSFP8_SWZ_SHIFT 1
-#endif
-__device__ __forceinline__ int swz_key(int r) { return (r >> DSFP8_SWZ_SHIFT) & 7; }
+// Byte offset of 16-byte chunk c of tile row r in LDS.  The chunk index is
+// XOR-ed with (r & 7) ^ ((r >> 3) & 1), which gives distinct chunks to the 8
+// rows of each aligned group of 8 and distinct (row parity, chunk) pairs to
+// the 16 rows of each aligned group of 16.  An MFMA fragment read (16
+// consecutive rows, one logical chunk) is then free of bank conflicts whether
+// the LDS serves it as 8 lanes over 128 bytes of banks or as 16 lanes over
+// 256 bytes (measured: no SQ_LDS_BANK_CONFLICT cycles, against 42% of the
+// LDS's active cycles with (r >> 1) & 7 or r & 7).  The key repeats every 16
+// rows, so all fragment reads of a wave share their lane offsets.
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ swz_key(r)) << 4); }
 
 // MFMA operand of one 16-row slice: lane (r, g) = (lane % 16, lane / 16) holds
@@ -450,20 +451,24 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   }
 
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
-  auto issue = [&](int kb, int stage) {
+  // Load n (0 .. LOADS-1) of K-block kb into `stage`: n < A_INSTR are A
+  // segments, then B segments, then the scale gather.  With live == false the
+  // A/B loads go to an out-of-range offset (reading zero into a stage nobody
+  // reads) and the gather re-reads K-block kb_safe, so a caller issuing past
+  // the last K-block needs no branch.
+  auto issue_one = [&](int n, int kb, int stage, bool live, int kb_safe) __attribute__((always_inline)) {
     const uint32_t st = lds0 + (uint32_t)(stage * CF::STAGE_BYTES);
     const int64_t kbyte = (int64_t)kb * BK;
-#pragma unroll
-    for (int i = 0; i < CF::A_INSTR; ++i) {
-      const uint32_t off = (kbyte + kcA[i] < K) ? offA[i] + (uint32_t)kbyte : kOob;
-      dma_b128(rsA, st + (uint32_t)((wave + NW * i) * 1024), off);
+    if (n < CF::A_INSTR) {
+      const uint32_t off = (live && kbyte + kcA[n] < K) ? offA[n] + (uint32_t)kbyte : kOob;
+      dma_b128(rsA, st + (uint32_t)((wave + NW * n) * 1024), off);
+    } else if (n < CF::A_INSTR + CF::B_INSTR) {
+      const int m = n - CF::A_INSTR;
+      const uint32_t off = (live && kbyte + kcB[m] < K) ? offB[m] + (uint32_t)kbyte : kOob;
+      dma_b128(rsB, st + (uint32_t)(CF::A_BYTES + (wave + NW * m) * 1024), off);
+    } else if (s_act) {
+      dma_gather_b32(st + (uint32_t)(CF::S_OFF + wave * CF::SAW * 4), sbase + (int64_t)kb_safe * sstep);
     }
-#pragma unroll
-    for (int i = 0; i < CF::B_INSTR; ++i) {
-      const uint32_t off = (kbyte + kcB[i] < K) ? offB[i] + (uint32_t)kbyte : kOob;
-      dma_b128(rsB, st + (uint32_t)(CF::A_BYTES + (wave + NW * i) * 1024), off);
-    }
-    if (s_act) dma_gather_b32(st + (uint32_t)(CF::S_OFF + wave * CF::SAW * 4), sbase + (int64_t)kb * sstep);
   };
 
   v4f acc[CF::TM][CF::TN];
@@ -476,14 +481,24 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   (void)nkb;
 #pragma unroll
   for (int s = 0; s < CF::STAGES - 1; ++s)
-    if (kb0 + s < kb1) issue(kb0 + s, s);
+    if (kb0 + s < kb1)
+#pragma unroll
+      for (int n = 0; n < CF::LOADS; ++n) issue_one(n, kb0 + s, s, true, kb0 + s);
 
+  // The loads of K-block kb + STAGES - 1 are spread over the row-subtile
+  // steps of kb (PER per step) instead of being issued together after the
+  // barrier: a burst of 8 waves x LOADS vector-memory instructions stalls
+  // instruction issue until the load unit has accepted them.
+  constexpr int PER = (CF::LOADS + CF::TM - 1) / CF::TM;
   const int fr = lane & 15, fg = lane >> 4;
   for (int kb = kb0; kb < kb1; ++kb) {
     const int later = (kb1 - 1 - kb) < (CF::STAGES - 2) ? (kb1 - 1 - kb) : (CF::STAGES - 2);
     wait_stage<CF>(later);
     __syncthreads();
-    if (kb + CF::STAGES - 1 < kb1) issue(kb + CF::STAGES - 1, (kb - kb0 + CF::STAGES - 1) % CF::STAGES);
+    const int kn = kb + CF::STAGES - 1;
+    const bool live = kn < kb1;
+    const int kn_safe = live ? kn : kb1 - 1;
+    const int slot = (kb - kb0 + CF::STAGES - 1) % CF::STAGES;
     const uint8_t* st = smem + ((kb - kb0) % CF::STAGES) * CF::STAGE_BYTES;
     const float* sarea = reinterpret_cast<const float*>(st + CF::S_OFF);
     const float bsv = sarea[wave * CF::SAW + CF::SA_ROWS];
@@ -508,17 +523,26 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
         for (int j = 0; j < CF::TN; ++j)
           part[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot, live, kn_safe);
       }
       if (i > 0) {
         const int r = i - 1;
 #pragma unroll
-        for (int j = 0; j < CF::TN; ++j)
+        for (int j = 0; j < CF::TN; ++j) {
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             acc[r][j][v] = __builtin_fmaf(part[r & 1][j][v], scv[r & 1][v], acc[r][j][v]);
+          // An empty statement that takes the new accumulators: the fmas stay
+          // here instead of being sunk to the end of the K-block, where all of
+          // the block's partial products would have to be live at once.
+          asm volatile("" ::"v"(acc[r][j][0]), "v"(acc[r][j][1]), "v"(acc[r][j][2]), "v"(acc[r][j][3]));
+        }
       }
     }
   }
+  // Loads issued for K-blocks past the end must land before the LDS is reused.
+  wait_vmcnt<0>();
   __syncthreads();
   if (t.partial != nullptr) {
     store_partial<CF>(p, t, acc, wm, wn, lane);
