@@ -121,9 +121,16 @@ struct TileRef {
   float* partial;        // non-null: store the fp32 partial [M, N] here instead of C
 };
 
+// Accumulator layouts of a 16 x 16 output subtile (i, j) of a wave, lane =
+// (fr, fg) = (lane % 16, lane / 16):
+//   row layout (activations as the MFMA's first operand): acc[i][j][v] is
+//     C[16i + 4fg + v][16j + fr];
+//   column layout (weights as the first operand): acc[i][j][v] is
+//     C[16i + fr][16j + 4fg + v], four consecutive columns of one row.
+
 // Epilogue: round to bf16, stage each wave's WM x WN tile in LDS (which the
 // caller has finished reading), then write rows of C with 16-byte stores.
-template <class CF>
+template <class CF, bool COLS>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, const v4f (&acc)[CF::TM][CF::TN],
                                            uint8_t* smem, int wave, int wm, int wn, int lane) {
   const int fr = lane & 15, fg = lane >> 4;
@@ -133,12 +140,20 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, 
 #pragma unroll
   for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::TN; ++j)
+    for (int j = 0; j < CF::TN; ++j) {
+      if constexpr (COLS) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<uint2*>(cst + (i * 16 + fr) * CS + j * 16 + 4 * fg) = w;
+      } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const __bf16 h = (__bf16)acc[i][j][v];
-        cst[(i * 16 + 4 * fg + v) * CS + j * 16 + fr] = __builtin_bit_cast(uint16_t, h);
+        for (int v = 0; v < 4; ++v) {
+          const __bf16 h = (__bf16)acc[i][j][v];
+          cst[(i * 16 + 4 * fg + v) * CS + j * 16 + fr] = __builtin_bit_cast(uint16_t, h);
+        }
       }
+    }
   __syncthreads();
   const int64_t crow0 = t.row0 + wm * CF::WM;
   const int64_t ccol0 = t.n0 + wn * CF::WN;
@@ -167,21 +182,37 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, 
 }
 
 // Split K: the fp32 partial of this tile goes straight from registers to the
-// workspace [M, N] of its split (16 lanes write 64 contiguous bytes).
-template <class CF>
+// workspace [M, N] of its split (row layout: 16 lanes write 64 contiguous
+// bytes; column layout: each lane writes 16 contiguous bytes).
+template <class CF, bool COLS>
 __device__ __forceinline__ void store_partial(const GemmArgs& p, const TileRef& t,
                                               const v4f (&acc)[CF::TM][CF::TN], int wm, int wn, int lane) {
   const int fr = lane & 15, fg = lane >> 4;
 #pragma unroll
   for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::TN; ++j)
+    for (int j = 0; j < CF::TN; ++j) {
+      if constexpr (COLS) {
+        const int64_t row = t.row0 + wm * CF::WM + i * 16 + fr;
+        const int64_t col = t.n0 + wn * CF::WN + j * 16 + 4 * fg;
+        if (row >= t.row_end) continue;
+        float* dst = t.partial + row * p.N + col;
+        if (col + 4 <= p.N && (p.N & 3) == 0) {
+          *reinterpret_cast<v4f*>(dst) = acc[i][j];
+        } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = t.row0 + wm * CF::WM + i * 16 + 4 * fg + v;
-        const int64_t col = t.n0 + wn * CF::WN + j * 16 + fr;
-        if (row < t.row_end && col < p.N) t.partial[row * p.N + col] = acc[i][j][v];
+          for (int v = 0; v < 4; ++v)
+            if (col + v < p.N) dst[v] = acc[i][j][v];
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = t.row0 + wm * CF::WM + i * 16 + 4 * fg + v;
+          const int64_t col = t.n0 + wn * CF::WN + j * 16 + fr;
+          if (row < t.row_end && col < p.N) t.partial[row * p.N + col] = acc[i][j][v];
+        }
       }
+    }
 }
 
 template <class CF, int VEC>
@@ -283,10 +314,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
 
   __syncthreads();
   if (t.partial != nullptr) {
-    store_partial<CF>(p, t, acc, wm, wn, lane);
+    store_partial<CF, false>(p, t, acc, wm, wn, lane);
     return;
   }
-  store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
+  store_tile<CF, false>(p, t, acc, smem, wave, wm, wn, lane);
 }
 
 // ---- direct-to-LDS pipeline (16-byte aligned operands) --------------------------------
@@ -316,10 +347,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+// Byte address of lane l: rsrc base + voff + soff (the scalar part carries the
+// K-block offset, so the per-lane offsets stay fixed over the K loop).
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory");
 }
 
@@ -356,8 +389,9 @@ struct DmaCfg {
   static constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
   static constexpr int LDS_BYTES = MAIN_BYTES > C_BYTES ? MAIN_BYTES : C_BYTES;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole 1 KB segments per wave");
-  static_assert(SA_ROWS >= 4 && SA_ROWS % 4 == 0 && SA_ROWS < 64 && BM % NW == 0, "scale rows per wave");
+  static_assert(SA_ROWS >= 16 && SA_ROWS % 16 == 0 && SA_ROWS < 64 && BM % NW == 0, "scale rows per wave");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-block");
+  static_assert(WM % SA_ROWS == 0, "a wave's rows start on a scale slot");
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
 };
 
@@ -405,7 +439,8 @@ __device__ __forceinline__ void wait_stage(int later) {
   wait_vmcnt<0>();
 }
 
-template <class CF>
+// KFULL: K is a multiple of 128, so no K-block has chunks past K.
+template <class CF, bool KFULL>
 __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
   constexpr int NW = CF::NW;
   const int tid = threadIdx.x;
@@ -413,7 +448,6 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
   const int64_t K = p.K, N = p.N;
-  const int nkb = (int)((K + BK - 1) / BK);
   const int64_t kbn = (N + BK - 1) / BK;
 
   const int64_t rowsA = t.row_end - t.row0 < CF::BM ? t.row_end - t.row0 : CF::BM;
@@ -425,11 +459,11 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   int64_t nbi = (t.n0 + wn * CF::WN) / BK;
   if (nbi > kbn - 1) nbi = kbn - 1;
   // Scale gather: lane l < SA_ROWS fetches a_s of tile row wave*SA_ROWS + l,
-  // lane SA_ROWS fetches b_s[nbi, kb]; K-block kb adds kb * stride.
+  // lane SA_ROWS fetches b_s[nbi, kb]; K-block kb adds kb * sstep bytes.
   const int srow = wave * CF::SA_ROWS + lane;
   const bool s_act = lane < CF::SA_ROWS ? srow < rowsA : lane == CF::SA_ROWS;
   const float* sbase = lane < CF::SA_ROWS ? t.a_s + (t.row0 + srow) * p.as_rs : t.b_s + nbi * p.ldbs;
-  const int64_t sstep = lane < CF::SA_ROWS ? p.as_ks : 1;
+  const uint32_t sstep = lane < CF::SA_ROWS ? (uint32_t)(p.as_ks * 4) : 4u;
 
   // Per-lane source offsets (K-block independent): lane -> LDS chunk (row r,
   // physical chunk lane % 8) <- logical chunk c of row r.
@@ -452,22 +486,24 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
   // Load n (0 .. LOADS-1) of K-block kb into `stage`: n < A_INSTR are A
-  // segments, then B segments, then the scale gather.  With live == false the
-  // A/B loads go to an out-of-range offset (reading zero into a stage nobody
-  // reads) and the gather re-reads K-block kb_safe, so a caller issuing past
-  // the last K-block needs no branch.
-  auto issue_one = [&](int n, int kb, int stage, bool live, int kb_safe) __attribute__((always_inline)) {
+  // segments, then B segments, then the scale gather.  Callers issuing past
+  // the last K-block pass the last one again (into a stage nobody reads), so
+  // no branch is needed.  Chunks past K (only in a last, partial K-block) go
+  // to an offset beyond the descriptor and read as zero.
+  auto issue_one = [&](int n, int kb, int stage) __attribute__((always_inline)) {
     const uint32_t st = lds0 + (uint32_t)(stage * CF::STAGE_BYTES);
-    const int64_t kbyte = (int64_t)kb * BK;
+    const uint32_t kbyte = (uint32_t)kb * BK;
     if (n < CF::A_INSTR) {
-      const uint32_t off = (live && kbyte + kcA[n] < K) ? offA[n] + (uint32_t)kbyte : kOob;
-      dma_b128(rsA, st + (uint32_t)((wave + NW * n) * 1024), off);
+      const uint32_t off = (KFULL || (int64_t)kbyte + kcA[n] < K) ? offA[n] : kOob;
+      dma_b128(rsA, st + (uint32_t)((wave + NW * n) * 1024), off, kbyte);
     } else if (n < CF::A_INSTR + CF::B_INSTR) {
       const int m = n - CF::A_INSTR;
-      const uint32_t off = (live && kbyte + kcB[m] < K) ? offB[m] + (uint32_t)kbyte : kOob;
-      dma_b128(rsB, st + (uint32_t)(CF::A_BYTES + (wave + NW * m) * 1024), off);
+      const uint32_t off = (KFULL || (int64_t)kbyte + kcB[m] < K) ? offB[m] : kOob;
+      dma_b128(rsB, st + (uint32_t)(CF::A_BYTES + (wave + NW * m) * 1024), off, kbyte);
     } else if (s_act) {
-      dma_gather_b32(st + (uint32_t)(CF::S_OFF + wave * CF::SAW * 4), sbase + (int64_t)kb_safe * sstep);
+      const float* src = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(sbase) +
+                                                        (uint64_t)(uint32_t)kb * sstep);
+      dma_gather_b32(st + (uint32_t)(CF::S_OFF + wave * CF::SAW * 4), src);
     }
   };
 
@@ -478,53 +514,71 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
     for (int j = 0; j < CF::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int kb0 = t.kb0, kb1 = t.kb1;
-  (void)nkb;
 #pragma unroll
   for (int s = 0; s < CF::STAGES - 1; ++s)
     if (kb0 + s < kb1)
 #pragma unroll
-      for (int n = 0; n < CF::LOADS; ++n) issue_one(n, kb0 + s, s, true, kb0 + s);
+      for (int n = 0; n < CF::LOADS; ++n) issue_one(n, kb0 + s, s);
+
+  // Fragment addressing.  Row R + fr of an operand tile (R a multiple of 16)
+  // keeps its logical chunk c at fr*128 + ((c ^ key(fr)) << 4) past row R, so
+  // a lane's two chunk offsets are fixed and each 16-row slice is a constant
+  // offset from the wave's base: the reads take immediate offsets.
+  const int fr = lane & 15, fg = lane >> 4;
+  const uint32_t fkey = (uint32_t)((fr & 7) ^ (fr >> 3));
+  const uint32_t lf0 = (uint32_t)(fr * BK) + ((((uint32_t)(2 * fg)) ^ fkey) << 4);
+  const uint32_t lf1 = (uint32_t)(fr * BK) + ((((uint32_t)(2 * fg + 1)) ^ fkey) << 4);
+  auto frag = [&](const uint8_t* base) __attribute__((always_inline)) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + lf0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + lf1);
+    v8i f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+  };
+  // The activation scale of row wm*WM + 16i + fr sits in slot row / SA_ROWS at
+  // index row % SA_ROWS; WM and 16i are whole multiples of 16, so the lane
+  // part is fr and the rest is a constant per subtile.
+  constexpr int SCALE_WAVE = CF::WM / CF::SA_ROWS * CF::SAW;
 
   // The loads of K-block kb + STAGES - 1 are spread over the row-subtile
   // steps of kb (PER per step) instead of being issued together after the
   // barrier: a burst of 8 waves x LOADS vector-memory instructions stalls
   // instruction issue until the load unit has accepted them.
   constexpr int PER = (CF::LOADS + CF::TM - 1) / CF::TM;
-  const int fr = lane & 15, fg = lane >> 4;
   for (int kb = kb0; kb < kb1; ++kb) {
     const int later = (kb1 - 1 - kb) < (CF::STAGES - 2) ? (kb1 - 1 - kb) : (CF::STAGES - 2);
     wait_stage<CF>(later);
     __syncthreads();
-    const int kn = kb + CF::STAGES - 1;
-    const bool live = kn < kb1;
-    const int kn_safe = live ? kn : kb1 - 1;
+    const int kn = kb + CF::STAGES - 1 < kb1 ? kb + CF::STAGES - 1 : kb1 - 1;
     const int slot = (kb - kb0 + CF::STAGES - 1) % CF::STAGES;
     const uint8_t* st = smem + ((kb - kb0) % CF::STAGES) * CF::STAGE_BYTES;
     const float* sarea = reinterpret_cast<const float*>(st + CF::S_OFF);
     const float bsv = sarea[wave * CF::SAW + CF::SA_ROWS];
-    const uint8_t* at = st;
-    const uint8_t* bt = st + CF::A_BYTES;
+    const uint8_t* at = st + wm * CF::WM * BK;
+    const uint8_t* bt = st + CF::A_BYTES + wn * CF::WN * BK;
+    const float* sl = sarea + wm * SCALE_WAVE + fr;
     v8i bfr[CF::TN];
 #pragma unroll
-    for (int j = 0; j < CF::TN; ++j) bfr[j] = read_frag(bt, wn * CF::WN + j * 16 + fr, fg);
-    // Row-subtile i's MFMAs are issued before the rescale of row-subtile
-    // i-1, so the fma of a partial product never waits for the MFMA that has
-    // just produced it.
+    for (int j = 0; j < CF::TN; ++j) bfr[j] = frag(bt + j * 16 * BK);
+    // The weight fragment is the MFMA's first operand, so a lane's four
+    // results of a subtile are four columns of one row (the column layout)
+    // and share one activation scale.  Row-subtile i's MFMAs are issued
+    // before the rescale of row-subtile i-1, so the fma of a partial product
+    // never waits for the MFMA that has just produced it.
     v4f part[2][CF::TN];
-    v4f scv[2];
+    float scv[2];
 #pragma unroll
     for (int i = 0; i <= CF::TM; ++i) {
       if (i < CF::TM) {
-        const v8i afr = read_frag(at, wm * CF::WM + i * 16 + fr, fg);
-        const int srow4 = wm * CF::WM + i * 16 + 4 * fg;  // first of this lane's 4 rows
-        scv[i & 1] =
-            *reinterpret_cast<const v4f*>(sarea + (srow4 / CF::SA_ROWS) * CF::SAW + srow4 % CF::SA_ROWS) * bsv;
+        const v8i afr = frag(at + i * 16 * BK);
+        scv[i & 1] = sl[(i * 16 / CF::SA_ROWS) * CF::SAW + (i * 16) % CF::SA_ROWS] * bsv;
 #pragma unroll
         for (int j = 0; j < CF::TN; ++j)
           part[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+              bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-        for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot, live, kn_safe);
+        for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
       }
       if (i > 0) {
         const int r = i - 1;
@@ -532,7 +586,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
         for (int j = 0; j < CF::TN; ++j) {
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            acc[r][j][v] = __builtin_fmaf(part[r & 1][j][v], scv[r & 1][v], acc[r][j][v]);
+            acc[r][j][v] = __builtin_fmaf(part[r & 1][j][v], scv[r & 1], acc[r][j][v]);
           // An empty statement that takes the new accumulators: the fmas stay
           // here instead of being sunk to the end of the K-block, where all of
           // the block's partial products would have to be live at once.
@@ -545,10 +599,10 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   wait_vmcnt<0>();
   __syncthreads();
   if (t.partial != nullptr) {
-    store_partial<CF>(p, t, acc, wm, wn, lane);
+    store_partial<CF, true>(p, t, acc, wm, wn, lane);
     return;
   }
-  store_tile<CF>(p, t, acc, smem, wave, wm, wn, lane);
+  store_tile<CF, true>(p, t, acc, smem, wave, wm, wn, lane);
 }
 
 // Workgroup i runs on XCD i % 8.  Renumber ids 0..total-1 so that each XCD
@@ -577,10 +631,12 @@ __device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t ti
 }
 
 // VEC > 0: the register-staged pipeline with VEC-byte loads (any alignment);
-// VEC == 0: the direct-to-LDS pipeline (16-byte aligned operands, K % 16 == 0).
+// VEC == 0 / -1: the direct-to-LDS pipeline (16-byte aligned operands,
+// K % 16 == 0) for K % 128 == 0 / otherwise.
 template <class CF, int VEC>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
-  if constexpr (VEC == 0) gemm_tile_dma<CF>(p, t, smem);
+  if constexpr (VEC == 0) gemm_tile_dma<CF, true>(p, t, smem);
+  else if constexpr (VEC == -1) gemm_tile_dma<CF, false>(p, t, smem);
   else gemm_tile<CF, VEC>(p, t, smem);
 }
 
@@ -757,15 +813,16 @@ __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) 
 
 inline bool aligned(const void* q, size_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; }
 
-// Load width for the operands: 0 selects the direct-to-LDS pipeline, which
-// needs 16-byte aligned rows, K % 16 == 0 and 32-bit tile offsets; otherwise
-// the widest aligned width for the register-staged pipeline.
+// Load width for the operands: 0 (K % 128 == 0) or -1 selects the
+// direct-to-LDS pipeline, which needs 16-byte aligned rows, K % 16 == 0,
+// 32-bit tile offsets and a 32-bit K-block step of the activation scales;
+// otherwise the widest aligned width for the register-staged pipeline.
 template <class CF>
 int pick_vec(const GemmArgs& a) {
   if (a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16) &&
       (int64_t)CF::BM * a.lda < ((int64_t)1 << 31) && (int64_t)CF::BN * a.ldb < ((int64_t)1 << 31) &&
-      true)
-    return 0;
+      a.as_ks < ((int64_t)1 << 29))
+    return a.K % BK == 0 ? 0 : -1;
   const int cands[3] = {16, 8, 4};
   for (int v : cands)
     if (a.K % v == 0 && a.lda % v == 0 && a.ldb % v == 0 && aligned(a.A, v) && aligned(a.B, v)) return v;
@@ -773,6 +830,14 @@ int pick_vec(const GemmArgs& a) {
 }
 
 #define DSFP8_LAUNCH(KERN, CF, VEC, GRID) hipLaunchKernelGGL((KERN<CF, VEC>), GRID, dim3(CF::kThreads), 0, s, a)
+// A direct-to-LDS launch, its K-tail variant chosen from K.
+#define DSFP8_LAUNCH_DMA(KERN, CF, GRID, STREAM, ARGS)                                       \
+  do {                                                                                       \
+    if ((ARGS).K % BK == 0)                                                                  \
+      hipLaunchKernelGGL((KERN<CF, 0>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);           \
+    else                                                                                     \
+      hipLaunchKernelGGL((KERN<CF, -1>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);          \
+  } while (0)
 
 template <class CFD, class CFG, bool GROUPED>
 hipError_t dispatch(const GemmArgs& a, dim3 gd, dim3 gg, hipStream_t s) {
@@ -780,6 +845,10 @@ hipError_t dispatch(const GemmArgs& a, dim3 gd, dim3 gg, hipStream_t s) {
     case 0:
       if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFD, 0, gd);
       else DSFP8_LAUNCH(gemm_kernel, CFD, 0, gd);
+      break;
+    case -1:
+      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFD, -1, gd);
+      else DSFP8_LAUNCH(gemm_kernel, CFD, -1, gd);
       break;
     case 16:
       if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFG, 16, gg);
@@ -845,8 +914,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
-  if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) == 0) {
-    hipLaunchKernelGGL((gemm_kernel<CfgDmaBig, 0>), dense_grid<CfgDmaBig>(a), dim3(CfgDmaBig::kThreads), 0, stream, a);
+  if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) <= 0) {
+    DSFP8_LAUNCH_DMA(gemm_kernel, CfgDmaBig, dense_grid<CfgDmaBig>(a), stream, a);
     return hipGetLastError();
   }
   return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);
@@ -859,7 +928,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
 // weight once per 256 rows instead of once per 64.
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.M == 0) return hipSuccess;
-  const bool dma = pick_vec<CfgGrp>(a) == 0 && pick_vec<CfgDmaBig>(a) == 0;
+  const bool dma = pick_vec<CfgGrp>(a) <= 0 && pick_vec<CfgDmaBig>(a) <= 0;
   ScheduleClasses cls{};
   if (dma) {
     cls.n = 3;
@@ -884,16 +953,13 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   c2.tile_start = a.tile_start + 2 * (E + 1);
   const int64_t s0 = mn(E, M), s1 = mn(E, M / (CfgGrp::BM + 1)), s2 = (M + CfgDmaBig::BM - 1) / CfgDmaBig::BM + mn(E, M / (CfgDma::BM + 1));
   if (s0 > 0) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<CfgGrp, 0>), dim3((unsigned)(s0 * tiles_n(CfgGrp::BN))),
-                       dim3(CfgGrp::kThreads), 0, stream, c0);
+    DSFP8_LAUNCH_DMA(grouped_gemm_kernel, CfgGrp, dim3((unsigned)(s0 * tiles_n(CfgGrp::BN))), stream, c0);
   }
   if (s1 > 0) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<CfgDma, 0>), dim3((unsigned)(s1 * tiles_n(CfgDma::BN))),
-                       dim3(CfgDma::kThreads), 0, stream, c1);
+    DSFP8_LAUNCH_DMA(grouped_gemm_kernel, CfgDma, dim3((unsigned)(s1 * tiles_n(CfgDma::BN))), stream, c1);
   }
   if (s2 > 0) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<CfgDmaBig, 0>), dim3((unsigned)(s2 * tiles_n(CfgDmaBig::BN))),
-                       dim3(CfgDmaBig::kThreads), 0, stream, c2);
+    DSFP8_LAUNCH_DMA(grouped_gemm_kernel, CfgDmaBig, dim3((unsigned)(s2 * tiles_n(CfgDmaBig::BN))), stream, c2);
   }
   return hipGetLastError();
 }

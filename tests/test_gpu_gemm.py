@@ -57,7 +57,9 @@ def test_ragged_ue8m0(layout):
 @pytest.mark.parametrize("layout", ["kb", "row"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (1, 256, 128), (129, 130, 300), (200, 64, 200), (65, 300, 100),
                                    (17, 129, 99), (128, 128, 256), (300, 520, 1544), (2, 2000, 16),
-                                   (257, 384, 640), (100, 1000, 4096)])
+                                   (257, 384, 640), (100, 1000, 4096),
+                                   # K % 16 == 0 with a partial last K-block (direct-to-LDS loads)
+                                   (64, 300, 400), (257, 384, 656), (300, 520, 1552)])
 def test_edge_shapes(M, N, K, layout):
     a, a_s, b, b_s = operands(M, N, K, I.TINY)
     check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, f"{M}x{N}x{K}")
@@ -69,6 +71,12 @@ def test_large_tile_path_with_tails(layout):
     # tiles in M (1300 = 5*256 + 20) and N (11000 = 42*256 + 248); full check.
     a, a_s, b, b_s = operands(1300, 11000, 640, I.TINY)
     check_gemm_full(run(a, a_s, b, b_s, layout), a, a_s, b, b_s, "1300x11000x640")
+
+
+def test_large_tile_path_partial_k_block():
+    # the 256 x 256 tiles with K = 5 * 128 + 80: the last K-block's chunks past K read as zero
+    a, a_s, b, b_s = operands(1300, 11000, 720, I.TINY)
+    check_gemm_full(run(a, a_s, b, b_s), a, a_s, b, b_s, "1300x11000x720")
 
 
 def test_layouts_bit_identical():

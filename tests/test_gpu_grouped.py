@@ -57,6 +57,7 @@ def _check_all(C, a, a_s, b, b_s, off, what):
     ([1] * 20, 256, 512),
     ([0, 0, 129, 0], 64, 1000),
     ([130, 127, 128, 1, 255], 384, 256),
+    ([70, 3, 300, 0, 129], 256, 272),  # partial last K-block on the direct-to-LDS path
 ])
 @pytest.mark.parametrize("layout", ["kb", "row"])
 def test_grouped_small(counts, N, K, layout):
