@@ -78,15 +78,15 @@ class Timer:
 
 # ---- dense FFN step ---------------------------------------------------------------------
 
-def setup_dense(dev):
+def setup_dense(dev, fmt="fp32"):
     d = I.WORKLOADS["dense_ffn"].dims
     M, D, F = d["M"], d["dim"], d["inter"]
     x = I.device_normal((M, D), seed=301, std=1.0, device=dev, dtype=torch.bfloat16)
     w13 = I.device_normal((2 * F, D), seed=302, std=0.02, device=dev)
-    q13, s13 = ds.weight_quant(w13)
+    q13, s13 = ds.weight_quant(w13, fmt)
     del w13
     w2 = I.device_normal((D, F), seed=303, std=0.02, device=dev)
-    q2, s2 = ds.weight_quant(w2)
+    q2, s2 = ds.weight_quant(w2, fmt)
     del w2
     bufs = dict(
         x=x, q13=q13, s13=s13, q2=q2, s2=s2,
@@ -98,16 +98,61 @@ def setup_dense(dev):
         out=torch.empty((M, D), dtype=torch.bfloat16, device=dev),
     )
     torch.cuda.synchronize()
-    return dict(M=M, D=D, F=F, b=bufs)
+    return dict(M=M, D=D, F=F, b=bufs, fmt=fmt)
 
 
 def dense_step(st, T):
-    b, F = st["b"], st["F"]
-    T.run("act_quant", lambda: ds.act_quant(b["x"], out=(b["xq"], b["xs"])))
-    T.run("gemm_up", lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"]))
+    b, F, fmt = st["b"], st["F"], st["fmt"]
+    T.run("act_quant", lambda: ds.act_quant(b["x"], fmt, out=(b["xq"], b["xs"])))
+    T.run("gemm_up", lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"], scale_fmt=fmt))
     T.run("silu_mul_act_quant",
-          lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:], out=(b["hq"], b["hs"])))
-    T.run("gemm_down", lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"]))
+          lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:], fmt, out=(b["hq"], b["hs"])))
+    T.run("gemm_down", lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"], scale_fmt=fmt))
+
+
+def run_dense(st, steps, warmup):
+    """Time `steps` dense FFN steps after `warmup`; returns (ms per step, Timer)."""
+    T = Timer()
+    for _ in range(warmup):
+        dense_step(st, T)
+    T.collect()
+    T.reset()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        dense_step(st, T)
+    s1.record()
+    T.collect()
+    torch.cuda.synchronize()
+    return s0.elapsed_time(s1) / steps, T
+
+
+def dense_kernels(st, T):
+    M, D, F = st["M"], st["D"], st["F"]
+    k = {}
+    for name, fl in (("gemm_up", 2.0 * M * 2 * F * D), ("gemm_down", 2.0 * M * D * F)):
+        us = T.avg_us(name)
+        k[name] = {"shape": [M, 2 * F if name == "gemm_up" else D, D if name == "gemm_up" else F],
+                   "us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
+                   "frac_of_fp8_peak": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+    for name, by in (("act_quant", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2))):
+        us = T.avg_us(name)
+        k[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
+                   "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}
+    return k
+
+
+def bench_dense_ue8m0(dev, steps):
+    """The dense step with power-of-two (ue8m0) scales throughout: the
+    products apply the scales inside the matrix instruction."""
+    st = setup_dense(dev, "ue8m0")
+    ms, T = run_dense(st, steps, 3)
+    M, D, F = st["M"], st["D"], st["F"]
+    flop = 2.0 * M * 2 * F * D + 2.0 * M * D * F
+    return {"workload": "dense FFN prefill with ue8m0 scales (same shapes)", "ms_per_step": round(ms, 4),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "kernels": dense_kernels(st, T)}
 
 
 def gemm_bytes(M, N, K):
@@ -225,7 +270,7 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     for i in range(copies + 3):
         ds.act_quant(x, fmt, out=(xq, xs))
-        ds.gemm(xq, xs, *ws[i % copies], out=out)
+        ds.gemm(xq, xs, *ws[i % copies], out=out, scale_fmt=fmt)
     torch.cuda.synchronize()
 
     # Kernels this short are timed as back-to-back launches between one event
@@ -241,7 +286,7 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
         return e0.elapsed_time(e1) * 1e3 / iters
 
     a_us = timed(lambda i: ds.act_quant(x, fmt, out=(xq, xs)))
-    g_us = timed(lambda i: ds.gemm(xq, xs, *ws[i % copies], out=out))
+    g_us = timed(lambda i: ds.gemm(xq, xs, *ws[i % copies], out=out, scale_fmt=fmt))
     fl, by = 2.0 * M * N * K, gemm_bytes(M, N, K)
     roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
     return {"workload": name, "gemm": {"us": round(g_us, 2), "tflops": round(fl / g_us / 1e6, 2),
@@ -380,36 +425,13 @@ def main():
     props = torch.cuda.get_device_properties(dev)
 
     st = setup_dense(dev)
-    T = Timer()
-    for _ in range(args.warmup):
-        dense_step(st, T)
-    T.collect()
-    T.reset()
-    torch.cuda.synchronize()
-    s0 = torch.cuda.Event(enable_timing=True)
-    s1 = torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(args.steps):
-        dense_step(st, T)
-    s1.record()
-    T.collect()
-    torch.cuda.synchronize()
-    step_ms = s0.elapsed_time(s1) / args.steps
+    step_ms, T = run_dense(st, args.steps, args.warmup)
 
     M, D, F = st["M"], st["D"], st["F"]
     fl_up, fl_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
     total_flop = fl_up + fl_dn
     value = total_flop / (step_ms * 1e-3) / 1e12
-    k = {}
-    for name, fl, by in (("gemm_up", fl_up, gemm_bytes(M, 2 * F, D)), ("gemm_down", fl_dn, gemm_bytes(M, D, F))):
-        us = T.avg_us(name)
-        k[name] = {"shape": [M, 2 * F if name == "gemm_up" else D, D if name == "gemm_up" else F],
-                   "us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
-                   "frac_of_fp8_peak": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
-    for name, by in (("act_quant", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2))):
-        us = T.avg_us(name)
-        k[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
-                   "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}
+    k = dense_kernels(st, T)
     up_us = T.avg_us("gemm_up")
     achieved = fl_up / up_us / 1e6
     traffic = recorded_traffic()
@@ -438,6 +460,9 @@ def main():
     }
     if not args.quick:
         others = {}
+        del st
+        torch.cuda.empty_cache()
+        others["dense_ffn_ue8m0"] = bench_dense_ue8m0(dev, 20)
         others["routed_experts"] = bench_moe(dev, 10)
         others["weight_dequant"] = bench_dequant(dev, 20)
         others["decode_qa"] = bench_small_gemm(dev, 50, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True)

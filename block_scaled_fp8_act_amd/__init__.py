@@ -179,8 +179,13 @@ def weight_dequant(q, S, out=None):
     return out
 
 
-def gemm(a, a_s, b, b_s, out=None):
-    """bf16 ``C [M, N] = A W^T`` with per-K-block scales (A e4m3 [M,K], W e4m3 [N,K])."""
+def gemm(a, a_s, b, b_s, out=None, scale_fmt="fp32"):
+    """bf16 ``C [M, N] = A W^T`` with per-K-block scales (A e4m3 [M,K], W e4m3 [N,K]).
+
+    ``scale_fmt="ue8m0"`` declares every scale a power of two (as produced by
+    the quantisers with that format); the matrix instruction then applies
+    them from their exponents.
+    """
     a = _mat(_bytes(a), "a", (torch.uint8,))
     b = _mat(_bytes(b), "b", (torch.uint8,))
     ars, aks = _scale_matrix(a_s, "a_s")
@@ -196,17 +201,18 @@ def gemm(a, a_s, b, b_s, out=None):
     wsb = lib.dsfp8_gemm_workspace_bytes(M, N, K)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device) if wsb else None
     st = lib.dsfp8_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, b.data_ptr(), _ld(b), b_s.data_ptr(),
-                        _ld(b_s), c.data_ptr(), _ld(c), M, N, K, ws.data_ptr() if ws is not None else None, wsb,
-                        _stream(a))
+                        _ld(b_s), c.data_ptr(), _ld(c), M, N, K, _fmt(scale_fmt),
+                        ws.data_ptr() if ws is not None else None, wsb, _stream(a))
     _check("gemm", st)
     return c
 
 
-def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None):
+def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None, scale_fmt="fp32"):
     """Per-expert product over row ranges: rows ``offsets[e]:offsets[e+1]`` of A use W[e].
 
     ``b`` is e4m3 ``[E, N, K]``, ``b_s`` fp32 ``[E, ceil(N/128), ceil(K/128)]``,
     ``offsets`` int32 ``[E+1]`` on the device.  Returns bf16 ``[M_total, N]``.
+    ``scale_fmt`` as for :func:`gemm`.
     """
     a = _mat(_bytes(a), "a", (torch.uint8,))
     b = _mat(_bytes(b), "b", (torch.uint8,), dim=3)
@@ -228,7 +234,7 @@ def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None):
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
     st = lib.dsfp8_grouped_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, b.data_ptr(), K, b_s.data_ptr(),
-                                kblocks(K), offsets.data_ptr(), E, M, N, K, c.data_ptr(), _ld(c),
+                                kblocks(K), offsets.data_ptr(), E, M, N, K, c.data_ptr(), _ld(c), _fmt(scale_fmt),
                                 workspace.data_ptr(), workspace.numel(), _stream(a))
     _check("grouped_gemm", st)
     return c

@@ -20,10 +20,10 @@ SIGNATURES = {
                                       _p]),
     "dsfp8_weight_quant": (_i, [_p, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _i, _p]),
     "dsfp8_weight_dequant": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
-    "dsfp8_gemm": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz, _p]),
+    "dsfp8_gemm": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _i, _p, _sz, _p]),
     "dsfp8_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "dsfp8_grouped_gemm": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p,
-                                _i64, _p, _sz, _p]),
+                                _i64, _i, _p, _sz, _p]),
     "dsfp8_grouped_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
 }
 

@@ -198,8 +198,10 @@ size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
                         const void* B, int64_t ldb, const float* b_s, int64_t ldbs, void* C, int64_t ldc, int64_t M,
-                        int64_t N, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        int64_t N, int64_t K, int scale_fmt, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
   DSFP8_TRY(check_mat(A, M, K, lda, 1));
   DSFP8_TRY(check_scales(a_s, M, nblk(K), as_row_stride, as_kb_stride));
   DSFP8_TRY(check_mat(B, N, K, ldb, 1));
@@ -225,6 +227,7 @@ dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as
   a.N = N;
   a.K = K;
   a.partial = static_cast<float*>(workspace);
+  a.pow2 = scale_fmt == DSFP8_SCALE_UE8M0;
   return launched(dsfp8::launch_gemm(a, stream));
 }
 
@@ -239,8 +242,10 @@ size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N,
 dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
                                 int64_t as_kb_stride, const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
                                 const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* C,
-                                int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                int64_t ldc, int scale_fmt, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   if (!dim_ok(M_total) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
   if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
   if (offsets == nullptr) return DSFP8_ERR_NULL;
   if (!al(offsets, 4)) return DSFP8_ERR_ALIGN;
@@ -272,6 +277,7 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   a.offsets = offsets;
   a.E = E;
   a.tile_start = static_cast<int32_t*>(workspace);
+  a.pow2 = scale_fmt == DSFP8_SCALE_UE8M0;
   return launched(dsfp8::launch_grouped_gemm(a, stream));
 }
 

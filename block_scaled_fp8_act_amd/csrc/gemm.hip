@@ -440,7 +440,15 @@ __device__ __forceinline__ void wait_stage(int later) {
 }
 
 // KFULL: K is a multiple of 128, so no K-block has chunks past K.
-template <class CF, bool KFULL>
+// POW2: every scale is a power of two.  The block-scaled form of the MFMA
+// then applies them: with the operand layout used here, lane l supplies the
+// E8M0 scale (the fp32 exponent field, value 2^(e-127)) of operand row l % 16
+// for the 32-byte K slice l / 16, and a 128-K-block's four slices share
+// their scale, so each lane passes its own row's exponent and the MFMA
+// accumulates straight into the accumulator.  (Without POW2 the scale
+// operands are the literal 0, for which the compiler emits the unscaled
+// instruction; a zero scale supplied at run time would mean 2^-127.)
+template <class CF, bool KFULL, bool POW2>
 __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
   constexpr int NW = CF::NW;
   const int tid = threadIdx.x;
@@ -566,6 +574,20 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
     // and share one activation scale.  Row-subtile i's MFMAs are issued
     // before the rescale of row-subtile i-1, so the fma of a partial product
     // never waits for the MFMA that has just produced it.
+    if constexpr (POW2) {
+      const int eb = (int)(__float_as_uint(bsv) >> 23);
+#pragma unroll
+      for (int i = 0; i < CF::TM; ++i) {
+        const v8i afr = frag(at + i * 16 * BK);
+        const int ea = (int)(__float_as_uint(sl[(i * 16 / CF::SA_ROWS) * CF::SAW + (i * 16) % CF::SA_ROWS]) >> 23);
+#pragma unroll
+        for (int j = 0; j < CF::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, acc[i][j], 0, 0, 0, eb, 0, ea);
+#pragma unroll
+        for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+      }
+      continue;
+    }
     v4f part[2][CF::TN];
     float scv[2];
 #pragma unroll
@@ -630,13 +652,14 @@ __device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t ti
   tn = in / gsize;
 }
 
-// VEC > 0: the register-staged pipeline with VEC-byte loads (any alignment);
-// VEC == 0 / -1: the direct-to-LDS pipeline (16-byte aligned operands,
-// K % 16 == 0) for K % 128 == 0 / otherwise.
+// VEC > 0: the register-staged pipeline with VEC-byte loads (any alignment;
+// power-of-two scales take the general fp32 path there);
+// VEC <= 0: the direct-to-LDS pipeline (16-byte aligned operands,
+// K % 16 == 0): 0 / -1 for K % 128 == 0 / otherwise, -2 / -3 the same with
+// power-of-two scales.
 template <class CF, int VEC>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
-  if constexpr (VEC == 0) gemm_tile_dma<CF, true>(p, t, smem);
-  else if constexpr (VEC == -1) gemm_tile_dma<CF, false>(p, t, smem);
+  if constexpr (VEC <= 0) gemm_tile_dma<CF, VEC == 0 || VEC == -2, VEC <= -2>(p, t, smem);
   else gemm_tile<CF, VEC>(p, t, smem);
 }
 
@@ -830,25 +853,26 @@ int pick_vec(const GemmArgs& a) {
 }
 
 #define DSFP8_LAUNCH(KERN, CF, VEC, GRID) hipLaunchKernelGGL((KERN<CF, VEC>), GRID, dim3(CF::kThreads), 0, s, a)
-// A direct-to-LDS launch, its K-tail variant chosen from K.
+// A direct-to-LDS launch, its variant chosen from K and the scale format.
 #define DSFP8_LAUNCH_DMA(KERN, CF, GRID, STREAM, ARGS)                                       \
   do {                                                                                       \
-    if ((ARGS).K % BK == 0)                                                                  \
-      hipLaunchKernelGGL((KERN<CF, 0>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);           \
-    else                                                                                     \
-      hipLaunchKernelGGL((KERN<CF, -1>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);          \
+    const bool kfull_ = (ARGS).K % BK == 0;                                                  \
+    if ((ARGS).pow2) {                                                                       \
+      if (kfull_) hipLaunchKernelGGL((KERN<CF, -2>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS); \
+      else hipLaunchKernelGGL((KERN<CF, -3>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);        \
+    } else {                                                                                 \
+      if (kfull_) hipLaunchKernelGGL((KERN<CF, 0>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);  \
+      else hipLaunchKernelGGL((KERN<CF, -1>), GRID, dim3(CF::kThreads), 0, STREAM, ARGS);        \
+    }                                                                                        \
   } while (0)
 
 template <class CFD, class CFG, bool GROUPED>
 hipError_t dispatch(const GemmArgs& a, dim3 gd, dim3 gg, hipStream_t s) {
   switch (pick_vec<CFD>(a)) {
     case 0:
-      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFD, 0, gd);
-      else DSFP8_LAUNCH(gemm_kernel, CFD, 0, gd);
-      break;
     case -1:
-      if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFD, -1, gd);
-      else DSFP8_LAUNCH(gemm_kernel, CFD, -1, gd);
+      if constexpr (GROUPED) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, CFD, gd, s, a);
+      else DSFP8_LAUNCH_DMA(gemm_kernel, CFD, gd, s, a);
       break;
     case 16:
       if constexpr (GROUPED) DSFP8_LAUNCH(grouped_gemm_kernel, CFG, 16, gg);

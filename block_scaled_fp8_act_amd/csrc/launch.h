@@ -61,6 +61,8 @@ struct GemmArgs {
   int32_t* tile_start;  // workspace: E+1 ints
   // dense form with split K: fp32 partial products [splits, M, N] (workspace)
   float* partial;
+  // every scale is a power of two: the MFMA applies them (exponents only)
+  bool pow2;
 };
 
 hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream);

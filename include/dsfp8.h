@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSFP8_ABI_VERSION 2
+#define DSFP8_ABI_VERSION 3
 #define DSFP8_BLOCK 128
 
 typedef int dsfp8_status;
@@ -185,14 +185,21 @@ dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t l
  *   B      e4m3 [N, K], row stride ldb (the weight)     (device, read)
  *   b_s    fp32 [KB(N), KB(K)], row stride ldbs         (device, read)
  *   C      bf16 [M, N], row stride ldc                  (device, written)
+ *   scale_fmt  DSFP8_SCALE_FP32: any positive finite scales.
+ *          DSFP8_SCALE_UE8M0: the caller guarantees that every a_s and b_s
+ *          value is a positive normal power of two (what act_quant and the
+ *          weight quantiser produce with that format, [UG] FAQ on
+ *          scale_fmt); only the exponent bits are read and the scaling is
+ *          done inside the matrix instruction (CDNA4's block-scaled MFMA).
+ *          The result definition is the same.
  *   workspace / workspace_bytes: scratch of at least
  *          dsfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
- * Errors: NULL, SHAPE, LD, ALIGN, WORKSPACE, LAUNCH.
+ * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, WORKSPACE, LAUNCH.
  */
 dsfp8_status dsfp8_gemm(const void* A, int64_t lda,
                         const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
                         const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
-                        void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int scale_fmt,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -217,15 +224,17 @@ size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *            so malformed offsets give unspecified output but no access
  *            outside A, a_s or C.  Experts with no rows cost nothing.
  *   C        bf16 [M_total, N], row stride ldc              (device, written)
+ *   scale_fmt  as for dsfp8_gemm.
  * The combine step (scatter-add of each row times its routing weight) is not
  * part of this call.
- * Errors: NULL, SHAPE (E < 1, or E > 65536), LD, ALIGN, WORKSPACE, LAUNCH.
+ * Errors: NULL, SHAPE (E < 1, or E > 65536), LD, ALIGN, SCALE_FMT, WORKSPACE,
+ * LAUNCH.
  */
 dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda,
                                 const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
                                 const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
                                 const int32_t* offsets, int64_t E, int64_t M_total,
-                                int64_t N, int64_t K, void* C, int64_t ldc,
+                                int64_t N, int64_t K, void* C, int64_t ldc, int scale_fmt,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K);

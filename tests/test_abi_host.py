@@ -104,8 +104,12 @@ def test_silu_and_weight_validation(lib):
 
 
 def test_gemm_validation(lib):
-    g = lib.dsfp8_gemm
-    # A, lda, a_s, as_rs, as_ks, B, ldb, b_s, ldbs, C, ldc, M, N, K, ws, wsb, stream
+    def g(*args, fmt=0):
+        # A, lda, a_s, as_rs, as_ks, B, ldb, b_s, ldbs, C, ldc, M, N, K, [scale_fmt], ws, wsb, stream
+        return lib.dsfp8_gemm(*args[:14], fmt, *args[14:])
+
+    assert g(P, 256, P, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None, fmt=2) == FMT
+    assert g(P, 256, P, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None, fmt=-1) == FMT
     assert g(P, 256, P, 2, 1, P, 256, P, 2, P, 64, -8, 64, 256, None, 0, None) == SHAPE
     assert g(None, 256, P, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == NULL
     assert g(P, 255, P, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == LD
@@ -127,8 +131,8 @@ def test_gemm_validation(lib):
 def test_grouped_validation(lib):
     g = lib.dsfp8_grouped_gemm
     names = ["A", "lda", "a_s", "as_rs", "as_ks", "B", "ldb", "b_s", "ldbs", "offsets", "E", "M", "N", "K", "C",
-             "ldc", "ws", "wsb", "stream"]
-    args = [P, 256, P, 1, 100, P, 256, P, 2, P, 4, 100, 64, 256, P, 64, P, 1 << 20, None]
+             "ldc", "fmt", "ws", "wsb", "stream"]
+    args = [P, 256, P, 1, 100, P, 256, P, 2, P, 4, 100, 64, 256, P, 64, 0, P, 1 << 20, None]
 
     def call(**kw):
         a = list(args)
@@ -136,6 +140,7 @@ def test_grouped_validation(lib):
             a[names.index(k)] = v
         return g(*a)
 
+    assert call(fmt=3) == FMT
     assert call(E=0) == SHAPE
     assert call(E=70000) == SHAPE
     assert call(offsets=None) == NULL

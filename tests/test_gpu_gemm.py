@@ -17,7 +17,7 @@ from oracle import formats as F
 from oracle import gemm as G
 from oracle import quant as Q
 
-from gpu_helpers import (check_gemm_full, check_product, dev_bf16, dev_f32, dev_scales, dev_u8,
+from gpu_helpers import (bf16_to_f64, check_gemm_full, check_product, dev_bf16, dev_f32, dev_scales, dev_u8,
                          host_bits16, host_u8)
 
 pytestmark = pytest.mark.gpu
@@ -30,8 +30,8 @@ def operands(M, N, K, cid, ue8m0=False, outliers=0.0):
     return a, a_s, b, b_s
 
 
-def run(a, a_s, b, b_s, layout="kb"):
-    c = ds.gemm(dev_u8(a), dev_scales(a_s, layout), dev_u8(b), dev_f32(b_s))
+def run(a, a_s, b, b_s, layout="kb", scale_fmt="fp32"):
+    c = ds.gemm(dev_u8(a), dev_scales(a_s, layout), dev_u8(b), dev_f32(b_s), scale_fmt=scale_fmt)
     torch.cuda.synchronize()
     return host_bits16(c)
 
@@ -96,7 +96,10 @@ def test_k_zero_writes_zeros():
     assert c.shape == (5, 7) and torch.all(c == 0)
 
 
-def test_integer_operands_bit_exact():
+@pytest.mark.parametrize("scale_fmt", ["fp32", "ue8m0"])
+def test_integer_operands_bit_exact(scale_fmt):
+    # The scales are powers of two, so the ue8m0 form (scales applied inside
+    # the matrix instruction, per row and 32-byte K slice) must agree too.
     g = np.random.default_rng(11)
     M, N, K = 200, 300, 1024
     ai = g.integers(-4, 5, (M, K))
@@ -105,12 +108,31 @@ def test_integer_operands_bit_exact():
     b = F.e4m3_encode(bi.astype(np.float32))
     a_s = np.ldexp(np.ones((M, 8), np.float32), g.integers(-3, 1, (M, 8))).astype(np.float32)
     b_s = np.ldexp(np.ones((3, 8), np.float32), g.integers(-3, 1, (3, 8))).astype(np.float32)
-    C = run(a, a_s, b, b_s)
+    C = run(a, a_s, b, b_s, scale_fmt=scale_fmt)
     ref = G.gemm(a, a_s, b, b_s)
     # Every partial sum is a multiple of 2^-6 of magnitude at most
     # 8 * 128 * 16 = 2^14, hence exact in fp32 in any order; the only rounding
     # left is the final one to bf16.
     assert np.array_equal(C, F.f32_to_bf16(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1300, 11000, 640),   # 256 x 256 tiles
+    (1300, 11000, 720),   # 256 x 256 tiles, partial last K-block
+    (257, 384, 656),      # 128 x 128 tiles, partial last K-block
+    (100, 1000, 4096),    # split K
+    (333, 2500, 1000),    # K % 16 != 0: register-staged pipeline (general fp32 path)
+])
+def test_ue8m0_scaled_product(M, N, K):
+    # power-of-two activation and weight scales, declared as such: checked
+    # against the oracle, and against the same product with fp32-format scales
+    a, a_s, b, b_s = operands(M, N, K, I.RAGGED, ue8m0=True)
+    C = run(a, a_s, b, b_s, scale_fmt="ue8m0")
+    check_gemm_full(C, a, a_s, b, b_s, f"ue8m0 {M}x{N}x{K}")
+    C32 = run(a, a_s, b, b_s)
+    A_hat = G.dequant_act(a, a_s)
+    W_hat = G.dequant_weight(b, b_s)
+    check_product(C, bf16_to_f64(C32), A_hat, W_hat, f"ue8m0 vs fp32 form {M}x{N}x{K}")
 
 
 def test_one_hot_weight():

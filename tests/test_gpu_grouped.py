@@ -22,13 +22,13 @@ from gpu_helpers import check_product, dev_f32, dev_scales, dev_u8, host_bits16,
 pytestmark = pytest.mark.gpu
 
 
-def _case(counts, N, K, seed):
+def _case(counts, N, K, seed, ue8m0=False):
     counts = np.asarray(counts)
     E = len(counts)
     M = int(counts.sum())
     x = I.activations((M, K), I.MOE, seed)
-    a, a_s = Q.act_quant(x)
-    qs = [Q.weight_quant(I.weights_f32((N, K), I.MOE, 1000 * seed + e)) for e in range(E)]
+    a, a_s = Q.act_quant(x, ue8m0=ue8m0)
+    qs = [Q.weight_quant(I.weights_f32((N, K), I.MOE, 1000 * seed + e), ue8m0=ue8m0) for e in range(E)]
     b = np.stack([q for q, _ in qs])
     b_s = np.stack([s for _, s in qs])
     off = np.zeros(E + 1, np.int32)
@@ -36,8 +36,9 @@ def _case(counts, N, K, seed):
     return a, a_s, b, b_s, off
 
 
-def _run(a, a_s, b, b_s, off, layout="kb"):
-    c = ds.grouped_gemm(dev_u8(a), dev_scales(a_s, layout), dev_u8(b), dev_f32(b_s), torch.from_numpy(off).cuda())
+def _run(a, a_s, b, b_s, off, layout="kb", scale_fmt="fp32"):
+    c = ds.grouped_gemm(dev_u8(a), dev_scales(a_s, layout), dev_u8(b), dev_f32(b_s), torch.from_numpy(off).cuda(),
+                        scale_fmt=scale_fmt)
     torch.cuda.synchronize()
     return host_bits16(c)
 
@@ -64,6 +65,16 @@ def test_grouped_small(counts, N, K, layout):
     a, a_s, b, b_s, off = _case(counts, N, K, len(counts))
     C = _run(a, a_s, b, b_s, off, layout)
     _check_all(C, a, a_s, b, b_s, off, f"{counts}")
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([5, 0, 17, 1, 0, 300, 9], 256, 512),
+    ([70, 3, 300, 0, 129], 256, 272),
+])
+def test_grouped_ue8m0(counts, N, K):
+    a, a_s, b, b_s, off = _case(counts, N, K, len(counts), ue8m0=True)
+    C = _run(a, a_s, b, b_s, off, scale_fmt="ue8m0")
+    _check_all(C, a, a_s, b, b_s, off, f"ue8m0 {counts}")
 
 
 def test_single_expert_equals_dense():
