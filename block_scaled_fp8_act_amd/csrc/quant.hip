@@ -9,7 +9,7 @@
 // that never leaves the row.  Each lane computes the block scale and its
 // correctly rounded reciprocal once, and every quotient x/s costs one multiply
 // and two fma.  Work is distributed as (row, block) units in a grid-stride
-// loop sized to the machine; each lane keeps UNITS independent 16-byte loads
+// loop sized to the machine; each lane keeps kUnroll independent 16-byte loads
 // in flight.
 #include "device.h"
 #include "launch.h"
@@ -18,7 +18,10 @@ namespace dsfp8 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+// Units in flight per lane.  Two (rather than four or eight) keeps the
+// register count low enough for more resident waves, which measured faster
+// for both the plain and the fused kernel.
+constexpr int kUnroll = 2;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -32,7 +35,9 @@ __device__ __forceinline__ u32x4 mk4(uint32_t a, uint32_t b, uint32_t c, uint32_
 // Activation quantisation of one (row, block) unit held by 16 lanes.
 // `v` holds this lane's 8 values (already SiLU-gated if fused); `valid` says
 // which of them are real columns.  Writes y, s (and nothing for padding).
-template <bool VEC>
+// NT: store y with the nontemporal hint (faster for the fused kernel, slower
+// for the plain one on large tensors, both measured).
+template <bool VEC, bool NT>
 __device__ __forceinline__ void quantise_unit(const float (&v)[8], int nvalid, const ActQuantArgs& a,
                                               int64_t m, int64_t b, int lane16, bool live) {
   float amax = 0.0f;
@@ -52,7 +57,8 @@ __device__ __forceinline__ void quantise_unit(const float (&v)[8], int nvalid, c
       u32x2 o;
       o.x = pack_e4m3x4(q[0], q[1], q[2], q[3]);
       o.y = pack_e4m3x4(q[4], q[5], q[6], q[7]);
-      *reinterpret_cast<u32x2*>(yrow + col) = o;
+      if (NT) __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(yrow + col));
+      else *reinterpret_cast<u32x2*>(yrow + col) = o;
     }
   } else {
     uint32_t lo = pack_e4m3x4(q[0], q[1], q[2], q[3]);
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int
           }
         }
       }
-      quantise_unit<VEC>(v, nvalid, a, ms[i], bs[i], lane16, live[i]);
+      quantise_unit<VEC, FUSED>(v, nvalid, a, ms[i], bs[i], lane16, live[i]);
     }
   }
 }
@@ -229,72 +235,71 @@ __global__ __launch_bounds__(kThreads) void weight_quant_kernel(WeightQuantArgs 
 // ---- weight dequantisation -----------------------------------------------------
 //
 // ("DeepSeek-V3 Administrator & Developer Guide", 8.5.2.)  Each lane converts
-// 16 consecutive e4m3 bytes of one row with eight v_cvt_pk_f32_fp8, multiplies
-// each value by the block's scale in fp32, rounds pairs to bf16 with eight
-// v_cvt_pk_bf16_f32 and stores 32 bytes.  A workgroup covers 4096 columns of
-// kDqRows rows.
+// 8 consecutive e4m3 bytes of a row with four v_cvt_pk_f32_fp8, multiplies
+// each value by the block's scale in fp32 and rounds pairs to bf16 with
+// v_cvt_pk_bf16_f32.  A lane handles two such column chunks 2048 apart in
+// each of kDqRows rows, so a wave's loads read 512 contiguous bytes and its
+// 16-byte stores write 1 KB contiguous (two 16-byte stores per lane 32 bytes
+// apart wrote each line half at a time and ran 22% slower).  A workgroup
+// covers 4096 columns of kDqRows rows.
 
 constexpr int kDqRows = 8;
 
-__device__ __forceinline__ void dequant16(const u32x4 w, float s, u32x4& o0, u32x4& o1) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-  uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], false);
-    f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], true);
-    out[2 * i] = pack_bf16x2(lo[0] * s, lo[1] * s);
-    out[2 * i + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
-  }
-  o0 = mk4(out[0], out[1], out[2], out[3]);
-  o1 = mk4(out[4], out[5], out[6], out[7]);
-}
-
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void weight_dequant_kernel(DequantArgs a) {
-  const int64_t col = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 16;
-  if (col >= a.K) return;
+  const int64_t cbase = (int64_t)blockIdx.x * (kThreads * 16) + threadIdx.x * 8;
   const int64_t row0 = (int64_t)blockIdx.y * kDqRows;
-  const int64_t kb = col / kBlock;
-  // All rows' loads are issued before any conversion, so kDqRows 16-byte
-  // loads per lane are in flight at once.
-  u32x4 w[kDqRows];
-  float sc[kDqRows];
+  u32x2 w[2][kDqRows];
+  float sc[2][kDqRows];
 #pragma unroll
-  for (int r = 0; r < kDqRows; ++r) {
-    const int64_t n = row0 + r;
-    const bool ok = n < a.N;
-    const int64_t nn = ok ? n : row0;
-    sc[r] = a.S[(nn / kBlock) * a.ldS + kb];
-    const uint8_t* src = a.w + nn * a.ldw + col;
-    if (VEC) {
-      w[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-    } else {
-      uint32_t bytes[16];
+  for (int h = 0; h < 2; ++h) {
+    const int64_t col = cbase + h * (kThreads * 8);
+    const int64_t cc = col < a.K ? col : 0;
+    const int64_t kb = cc / kBlock;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) bytes[j] = (col + j < a.K) ? src[j] : 0u;
-      w[r] = mk4(bytes[0] | bytes[1] << 8 | bytes[2] << 16 | bytes[3] << 24,
-                 bytes[4] | bytes[5] << 8 | bytes[6] << 16 | bytes[7] << 24,
-                 bytes[8] | bytes[9] << 8 | bytes[10] << 16 | bytes[11] << 24,
-                 bytes[12] | bytes[13] << 8 | bytes[14] << 16 | bytes[15] << 24);
+    for (int r = 0; r < kDqRows; ++r) {
+      const int64_t n = row0 + r;
+      const int64_t nn = n < a.N ? n : row0;
+      sc[h][r] = a.S[(nn / kBlock) * a.ldS + kb];
+      const uint8_t* src = a.w + nn * a.ldw + cc;
+      if (VEC) {
+        w[h][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+      } else {
+        uint32_t bytes[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bytes[j] = (col + j < a.K) ? src[j] : 0u;
+        w[h][r].x = bytes[0] | bytes[1] << 8 | bytes[2] << 16 | bytes[3] << 24;
+        w[h][r].y = bytes[4] | bytes[5] << 8 | bytes[6] << 16 | bytes[7] << 24;
+      }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kDqRows; ++r) {
-    const int64_t n = row0 + r;
-    if (n >= a.N) break;
-    u32x4 o0, o1;
-    dequant16(w[r], sc[r], o0, o1);
-    uint16_t* dst = a.out + n * a.ldo + col;
-    if (VEC) {
-      __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(dst));
-      __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(dst) + 1);
-    } else {
-      const uint32_t outw[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+  for (int h = 0; h < 2; ++h) {
+    const int64_t col = cbase + h * (kThreads * 8);
+    if (col >= a.K) continue;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (col + j < a.K) dst[j] = (uint16_t)((outw[j >> 1] >> (16 * (j & 1))) & 0xffff);
+    for (int r = 0; r < kDqRows; ++r) {
+      const int64_t n = row0 + r;
+      if (n >= a.N) break;
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const float s = sc[h][r];
+      const uint32_t words[2] = {w[h][r].x, w[h][r].y};
+      uint32_t out[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], false);
+        f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], true);
+        out[2 * i] = pack_bf16x2(lo[0] * s, lo[1] * s);
+        out[2 * i + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+      }
+      uint16_t* dst = a.out + n * a.ldo + col;
+      if (VEC) {
+        __builtin_nontemporal_store(mk4(out[0], out[1], out[2], out[3]), reinterpret_cast<u32x4*>(dst));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (col + j < a.K) dst[j] = (uint16_t)((out[j >> 1] >> (16 * (j & 1))) & 0xffff);
+      }
     }
   }
 }
@@ -307,6 +312,7 @@ hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.K == 0) return hipSuccess;
   const int64_t nb = (a.K + kBlock - 1) / kBlock;
   const int64_t G = (a.M + 3) / 4;  // groups of four rows
+  const int64_t units = G * nb;
   const FastDiv gdiv = make_fastdiv((uint32_t)G);
   const bool fused = a.u != nullptr;
   // 16-byte loads of x (and u), 8-byte stores of y, 16-byte stores of h.
@@ -314,12 +320,13 @@ hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
   if (fused) vec = vec && aligned(a.u, 16) && (a.ldu % 8 == 0);
   if (a.h) vec = vec && aligned(a.h, 16) && (a.ldh % 8 == 0);
   const int64_t waves_per_wg = kThreads / 64;
-  const int64_t want = (G * nb + waves_per_wg * kUnroll - 1) / (waves_per_wg * kUnroll);
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t want = (units + waves_per_wg * kUnroll - 1) / (waves_per_wg * kUnroll);
+  // Workgroups per CU (measured): 16 for the plain kernel, 8 for the fused one.
+  const int64_t cap = (int64_t)device_cu_count() * (fused ? 8 : 16);
   const int64_t grid = want < cap ? want : cap;
   // The multiply-shift division needs every wave-unit index the loop forms
   // (up to kUnroll grid-widths past the end) below 2^31.
-  const bool fast = G * nb + (int64_t)kUnroll * grid * waves_per_wg < ((int64_t)1 << 31);
+  const bool fast = units + (int64_t)kUnroll * grid * waves_per_wg < ((int64_t)1 << 31);
   dim3 g((unsigned)grid), blk(kThreads);
   if (fused) {
     if (vec) hipLaunchKernelGGL((act_quant_kernel<true, true>), g, blk, 0, stream, a, nb, gdiv, fast);
