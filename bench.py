@@ -144,6 +144,49 @@ def dense_kernels(st, T):
     return k
 
 
+def bench_bf16_path(dev, steps):
+    """The pages' default (bf16) path for the same dense FFN step, as a
+    comparison: each linear dequantises its e4m3 weight with weight_dequant
+    and multiplies in bf16 (the vendor library's GEMM through
+    torch.mm, a two-dimensional product); the gate is SiLU(w1 x) * (w3 x) in bf16."""
+    st = setup_dense(dev)
+    b, M, D, F = st["b"], st["M"], st["D"], st["F"]
+    w13 = torch.empty((2 * F, D), dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty((D, F), dtype=torch.bfloat16, device=dev)
+    T = Timer()
+
+    def step():
+        T.run("dequant_w13", lambda: ds.weight_dequant(b["q13"], b["s13"], out=w13))
+        T.run("gemm_up_bf16", lambda: torch.mm(b["x"], w13.t(), out=b["h13"]))
+        h = torch.nn.functional.silu(b["h13"][:, :F]) * b["h13"][:, F:]
+        T.run("dequant_w2", lambda: ds.weight_dequant(b["q2"], b["s2"], out=w2))
+        T.run("gemm_down_bf16", lambda: torch.mm(h, w2.t(), out=b["out"]))
+
+    for _ in range(3):
+        step()
+    T.collect()
+    T.reset()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        step()
+    s1.record()
+    T.collect()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    flop = 2.0 * M * 2 * F * D + 2.0 * M * D * F
+    out = {"workload": "dense FFN prefill, bf16 path (weight_dequant + bf16 GEMM per linear)",
+           "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    for name, fl in (("gemm_up_bf16", 2.0 * M * 2 * F * D), ("gemm_down_bf16", 2.0 * M * D * F)):
+        us = T.avg_us(name)
+        out[name] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1)}
+    for name in ("dequant_w13", "dequant_w2"):
+        out[name] = {"us": round(T.avg_us(name), 1)}
+    return out
+
+
 def bench_dense_ue8m0(dev, steps):
     """The dense step with power-of-two (ue8m0) scales throughout: the
     products apply the scales inside the matrix instruction."""
@@ -463,6 +506,9 @@ def main():
         del st
         torch.cuda.empty_cache()
         others["dense_ffn_ue8m0"] = bench_dense_ue8m0(dev, 20)
+        torch.cuda.empty_cache()
+        others["dense_ffn_bf16_path"] = bench_bf16_path(dev, 10)
+        torch.cuda.empty_cache()
         others["routed_experts"] = bench_moe(dev, 10)
         others["weight_dequant"] = bench_dequant(dev, 20)
         others["decode_qa"] = bench_small_gemm(dev, 50, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True)

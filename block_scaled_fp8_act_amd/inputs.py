@@ -91,12 +91,13 @@ def device_normal(shape, seed, std, device, dtype=torch.float32):
     return t.to(dtype)
 
 
-def zipf_routing(tokens, experts, topk, s, cid=MOE, seed=SEED):
-    """Top-k expert choice per token with Zipf(s) popularity.
+def zipf_topk(tokens, experts, topk, s, cid=MOE, seed=SEED):
+    """Synthetic gate output: per token, ``topk`` distinct experts drawn with
+    Zipf(s) popularity (Gumbel top-k over log-popularity), and positive routing
+    weights (uniform draws normalised to sum 1 per token, times 2.5, the
+    routing scale of the 671B configuration) rounded to bf16.
 
-    Returns ``(token_of_row, offsets, counts)``: the (token, expert) pairs
-    sorted stably by expert, as the token index of each row, the int32
-    exclusive prefix sum of per-expert counts (length experts+1), and counts.
+    Returns ``(indices int32 [tokens, topk], weights_bits uint16 [tokens, topk])``.
     """
     g = rng(cid, 100, seed)
     perm = g.permutation(experts)                  # expert perm[r] has rank r+1
@@ -105,13 +106,9 @@ def zipf_routing(tokens, experts, topk, s, cid=MOE, seed=SEED):
     gumbel = -np.log(-np.log(g.random((tokens, experts))))
     keys = logp[None, :] + gumbel
     choice = np.argpartition(-keys, topk - 1, axis=1)[:, :topk]   # distinct experts per token
-    tok = np.repeat(np.arange(tokens), topk)
-    exp = choice.reshape(-1)
-    order = np.argsort(exp, kind="stable")
-    counts = np.bincount(exp, minlength=experts)
-    offsets = np.zeros(experts + 1, dtype=np.int32)
-    offsets[1:] = np.cumsum(counts)
-    return tok[order].astype(np.int64), offsets, counts
+    w = g.uniform(0.05, 1.0, (tokens, topk))
+    w = 2.5 * w / w.sum(axis=1, keepdims=True)
+    return choice.astype(np.int32), to_bf16_bits(w.astype(np.float32))
 
 
 def random_offsets(total, experts, cid, tensor, empty_frac=0.25, seed=SEED):

@@ -22,6 +22,9 @@ What it computes, and where the pages define it:
   6.4 and 8.4).
 * ``glue``     -- SiLU(g) * u between the up and down projections
   (Admin Guide 1.2, MLP / Expert rows).
+* ``moe``      -- the routed-expert steps around the grouped product: the row
+  order of the (token, slot) pairs, the gathered act_quant and the weighted
+  bf16 combine (Admin Guide 6.4 and 8.4).
 
 Precision: the pages fix fp32 for the quantisers ("load ... as float32"), so
 those run in IEEE binary32 through NumPy float32 scalars/arrays, whose
@@ -34,6 +37,6 @@ pinned only against fp64 closed forms at a few points and a Fraction-free
 second evaluation; see its docstring.
 """
 
-from . import formats, quant, gemm, glue  # noqa: F401
+from . import formats, quant, gemm, glue, moe  # noqa: F401
 
 BLOCK = 128

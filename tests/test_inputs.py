@@ -19,19 +19,18 @@ def test_outlier_channels():
     assert np.sum(col_rms > 8) == 72
 
 
-def test_zipf_routing_structure():
-    tok, off, counts = I.zipf_routing(4096, 256, 8, 1.1)
-    assert off[0] == 0 and off[-1] == 4096 * 8 and np.all(np.diff(off) >= 0)
-    assert counts.max() <= 4096 and counts.sum() == 32768
+def test_zipf_topk_structure():
+    idx, w = I.zipf_topk(4096, 256, 8, 1.1)
+    assert idx.shape == (4096, 8) and idx.dtype == np.int32 and w.shape == (4096, 8) and w.dtype == np.uint16
+    assert idx.min() >= 0 and idx.max() < 256
     # each token picks 8 distinct experts
-    pairs = set()
-    for e in range(256):
-        for t in tok[off[e]:off[e + 1]]:
-            assert (t, e) not in pairs
-            pairs.add((t, e))
-    assert len(pairs) == 32768
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])
     # skewed popularity: the largest expert is far above the median
-    assert counts.max() > 20 * np.median(counts)
+    counts = np.bincount(idx.ravel(), minlength=256)
+    assert counts.sum() == 32768 and counts.max() > 20 * np.median(counts)
+    # positive bf16 weights summing to about 2.5 per token
+    wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(wf > 0) and np.allclose(wf.sum(axis=1), 2.5, rtol=2e-2)
 
 
 def test_random_offsets():
