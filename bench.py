@@ -209,13 +209,18 @@ def aq_bytes(M, K, inputs=1):
 # ---- other workloads ----------------------------------------------------------------------
 
 def bench_moe(dev, iters):
+    """The routed-expert step on the device: routing of the gate's top-k
+    choice, act_quant of the routed rows (gathered in the kernel), the grouped
+    [w1;w3] product, the fused SiLU gate and act_quant, the grouped w2 product
+    and the weighted bf16 combine into the token outputs."""
     d = I.WORKLOADS["moe"].dims
-    E, D, F = d["experts"], d["dim"], d["inter"]
-    tok, off, counts = I.zipf_routing(d["tokens"], E, d["topk"], d["zipf_s"])
-    M = int(off[-1])
-    xt = I.device_normal((d["tokens"], D), seed=401, std=1.0, device=dev, dtype=torch.bfloat16)
-    x = xt[torch.from_numpy(tok).to(dev)].contiguous()
-    del xt
+    E, D, F, Tk, k = d["experts"], d["dim"], d["inter"], d["tokens"], d["topk"]
+    idx_h, w_h = I.zipf_topk(Tk, E, k, d["zipf_s"])
+    idx = torch.from_numpy(idx_h).to(dev)
+    wts = torch.from_numpy(w_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    counts = np.bincount(idx_h.ravel(), minlength=E)
+    M = Tk * k
+    x = I.device_normal((Tk, D), seed=401, std=1.0, device=dev, dtype=torch.bfloat16)
     q13 = torch.empty((E, 2 * F, D), dtype=torch.uint8, device=dev)
     s13 = torch.empty((E, kb(2 * F), kb(D)), dtype=torch.float32, device=dev)
     q2 = torch.empty((E, D, F), dtype=torch.uint8, device=dev)
@@ -230,29 +235,48 @@ def bench_moe(dev, iters):
         q2[e].copy_(q)
         s2[e].copy_(s)
     del w, q, s
-    offd = torch.from_numpy(off).to(dev)
+    lib = ds._lib.load()
+    offd = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(M, dtype=torch.int32, device=dev)
+    token_rows = torch.empty((Tk, k), dtype=torch.int32, device=dev)
+    rws = torch.empty(lib.dsfp8_moe_route_workspace_bytes(Tk, k, E), dtype=torch.uint8, device=dev)
     xq = torch.empty((M, D), dtype=torch.uint8, device=dev)
     xs = ds.new_scales(M, kb(D), dev)
     h13 = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
     hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
     hs = ds.new_scales(M, kb(F), dev)
-    out = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(ds._lib.load().dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
+    yr = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((Tk, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
     T = Timer()
 
+    def route():
+        st = lib.dsfp8_moe_route(idx.data_ptr(), Tk, k, k, E, offd.data_ptr(), row_token.data_ptr(),
+                                 token_rows.data_ptr(), rws.data_ptr(), rws.numel(), stream)
+        assert st == 0, st
+
     def step():
-        T.run("act_quant", lambda: ds.act_quant(x, out=(xq, xs)))
+        T.run("route", route)
+        T.run("act_quant_rows", lambda: ds.act_quant_rows(x, row_token, out=(xq, xs)))
         T.run("grouped_up", lambda: ds.grouped_gemm(xq, xs, q13, s13, offd, out=h13, workspace=ws))
         T.run("silu_mul_act_quant", lambda: ds.silu_mul_act_quant(h13[:, :F], h13[:, F:], out=(hq, hs)))
-        T.run("grouped_down", lambda: ds.grouped_gemm(hq, hs, q2, s2, offd, out=out, workspace=ws))
+        T.run("grouped_down", lambda: ds.grouped_gemm(hq, hs, q2, s2, offd, out=yr, workspace=ws))
+        T.run("combine", lambda: ds.moe_combine(yr, idx, wts, token_rows, out=y))
 
     for _ in range(2):
         step()
     T.collect()
     T.reset()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
     for _ in range(iters):
         step()
+    s1.record()
     T.collect()
+    torch.cuda.synchronize()
     flop_up, flop_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
     by_up = M * D + E * 2 * F * D + 4 * (M * kb(D) + E * kb(2 * F) * kb(D)) + 2 * M * 2 * F
     by_dn = M * F + E * D * F + 4 * (M * kb(F) + E * kb(D) * kb(F)) + 2 * M * D
@@ -264,12 +288,15 @@ def bench_moe(dev, iters):
         roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
         res[name] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
                      "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3)}
-    for name, by in (("act_quant", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2))):
+    # act_quant_rows reads the routed rows of x (2 B), writes e4m3 and scales;
+    # combine reads the expert outputs and writes the token outputs (bf16).
+    for name, by in (("act_quant_rows", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2)),
+                     ("combine", 2 * M * D + 2 * Tk * D + Tk * k * 10)):
         us = T.avg_us(name)
         res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                      "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
-    step_us = sum(T.avg_us(n) for n in ("act_quant", "grouped_up", "silu_mul_act_quant", "grouped_down"))
-    res["step_us"] = round(step_us, 1)
+    res["route"] = {"us": round(T.avg_us("route"), 1)}
+    res["step_us"] = round(s0.elapsed_time(s1) * 1e3 / iters, 1)
     del q13, q2
     return res
 

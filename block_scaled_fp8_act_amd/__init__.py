@@ -238,3 +238,75 @@ def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None, scale_fmt="f
                                 workspace.data_ptr(), workspace.numel(), _stream(a))
     _check("grouped_gemm", st)
     return c
+
+
+# ---- routed experts ------------------------------------------------------------------
+
+def act_quant_rows(x, rows, scale_fmt="fp32", out=None):
+    """``act_quant(x[rows])`` without forming the gathered copy: e4m3 ``[len(rows), K]``
+    and its scales.  ``rows`` is an int32 CUDA tensor; entries are clamped to
+    ``[0, x.shape[0])``."""
+    x = _mat(x, "x", (torch.bfloat16,))
+    if not rows.is_cuda or rows.dtype != torch.int32 or rows.dim() != 1 or not rows.is_contiguous():
+        raise Dsfp8Error("rows must be a contiguous int32 CUDA tensor")
+    T, K = x.shape
+    M = rows.numel()
+    y, s = (None, None) if out is None else out
+    y = _out(y, (M, K), torch.uint8, x.device, "y")
+    s = _scales_out(s, M, kblocks(K), x.device)
+    srs, sks = _scale_strides(s)
+    st = _lib.load().dsfp8_act_quant_rows(x.data_ptr(), T, _ld(x), rows.data_ptr(), M, K, y.data_ptr(), _ld(y),
+                                          s.data_ptr(), srs, sks, _fmt(scale_fmt), _stream(x))
+    _check("act_quant_rows", st)
+    return y, s
+
+
+def _int32_mat(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or t.dim() != 2:
+        raise Dsfp8Error(f"{name} must be a 2-D int32 CUDA tensor")
+    if t.numel() > 0 and t.stride(-1) != 1:
+        raise Dsfp8Error(f"Input tensor must be contiguous in its last dimension ({name})")
+    return t
+
+
+def moe_route(indices, experts):
+    """Row order of the grouped product for the gate's ``indices [T, k]`` (int32).
+
+    Returns ``(offsets int32 [E+1], row_token int32 [T*k], token_rows int32 [T, k])``:
+    rows ``offsets[e]:offsets[e+1]`` are expert e's (token, slot) pairs in row-major
+    order, ``row_token[r]`` is the token of row r and ``token_rows[t, j]`` the row
+    of pair (t, j) (-1 when its index is outside ``[0, E)``).
+    """
+    indices = _int32_mat(indices, "indices")
+    T, k = indices.shape
+    lib = _lib.load()
+    dev = indices.device
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
+    token_rows = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wsb = lib.dsfp8_moe_route_workspace_bytes(T, k, experts)
+    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    st = lib.dsfp8_moe_route(indices.data_ptr(), T, k, _ld(indices), experts, offsets.data_ptr(),
+                             row_token.data_ptr(), token_rows.data_ptr(), ws.data_ptr(), ws.numel(), _stream(indices))
+    _check("moe_route", st)
+    return offsets, row_token, token_rows
+
+
+def moe_combine(yr, indices, weights, token_rows, out=None):
+    """bf16 ``[T, D]``: per token, the bf16 sum over its experts (in increasing
+    index) of ``bf16(yr[token_rows[t, j]] * weights[t, j])``, as the pages' loop
+    accumulates ``y[idx] += expert(x[idx]) * weights[idx, top]``."""
+    yr = _mat(yr, "yr", (torch.bfloat16,))
+    indices = _int32_mat(indices, "indices")
+    weights = _mat(weights, "weights", (torch.bfloat16,))
+    token_rows = _int32_mat(token_rows, "token_rows")
+    T, k = indices.shape
+    if tuple(weights.shape) != (T, k) or tuple(token_rows.shape) != (T, k) or not token_rows.is_contiguous():
+        raise Dsfp8Error("weights and token_rows must be [T, k] (token_rows contiguous) like indices")
+    R, D = yr.shape
+    out = _out(out, (T, D), torch.bfloat16, yr.device, "out")
+    st = _lib.load().dsfp8_moe_combine(yr.data_ptr(), R, _ld(yr), indices.data_ptr(), _ld(indices),
+                                       weights.data_ptr(), _ld(weights), token_rows.data_ptr(), T, k, D,
+                                       out.data_ptr(), _ld(out), _stream(yr))
+    _check("moe_combine", st)
+    return out

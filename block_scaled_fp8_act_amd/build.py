@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsfp8.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "moe.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -281,4 +281,88 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   return launched(dsfp8::launch_grouped_gemm(a, stream));
 }
 
+dsfp8_status dsfp8_act_quant_rows(const void* x, int64_t x_rows, int64_t ldx, const int32_t* rows, int64_t M,
+                                  int64_t K, void* y, int64_t ldy, float* s, int64_t s_row_stride,
+                                  int64_t s_kb_stride, int scale_fmt, hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(K) || !dim_ok(x_rows)) return DSFP8_ERR_SHAPE;
+  if (M > 0 && K > 0 && x_rows == 0) return DSFP8_ERR_SHAPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
+  DSFP8_TRY(check_mat(x, x_rows, K, ldx, 2));
+  if (M > 0 && rows == nullptr) return DSFP8_ERR_NULL;
+  if (!al(rows, 4)) return DSFP8_ERR_ALIGN;
+  DSFP8_TRY(check_quant_out(M, K, y, ldy, s, s_row_stride, s_kb_stride));
+  dsfp8::ActQuantArgs a{};
+  a.g = static_cast<const uint16_t*>(x);
+  a.ldg = ldx;
+  a.M = M;
+  a.K = K;
+  a.y = static_cast<uint8_t*>(y);
+  a.ldy = ldy;
+  a.s = s;
+  a.s_rs = s_row_stride;
+  a.s_ks = s_kb_stride;
+  a.ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
+  a.rows = rows;
+  a.g_rows = x_rows;
+  return launched(dsfp8::launch_act_quant(a, stream));
+}
+
+size_t dsfp8_moe_route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
+  if (!dim_ok(T) || k < 1 || k > 16 || E < 1 || E > dsfp8::kMaxRouteExperts) return 0;
+  if (T * k >= kMaxDim) return 0;
+  return dsfp8::route_workspace_bytes(T * k, E);
+}
+
+dsfp8_status dsfp8_moe_route(const int32_t* indices, int64_t T, int64_t k, int64_t ldi, int64_t E, int32_t* offsets,
+                             int32_t* row_token, int32_t* token_rows, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!dim_ok(T) || k < 1 || k > 16 || E < 1 || E > dsfp8::kMaxRouteExperts) return DSFP8_ERR_SHAPE;
+  if (T * k >= kMaxDim) return DSFP8_ERR_SHAPE;
+  DSFP8_TRY(check_mat(indices, T, k, ldi, 4));
+  DSFP8_TRY(check_mat(token_rows, T, k, k, 4));
+  DSFP8_TRY(check_mat(row_token, T * k, 1, 1, 4));
+  DSFP8_TRY(check_mat(offsets, E + 1, 1, 1, 4));
+  const size_t need = dsfp8_moe_route_workspace_bytes(T, k, E);
+  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
+  if (workspace == nullptr) return DSFP8_ERR_NULL;
+  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
+  dsfp8::RouteArgs a{};
+  a.indices = indices;
+  a.ldi = ldi;
+  a.k = k;
+  a.n = T * k;
+  a.E = (int)E;
+  a.offsets = offsets;
+  a.row_token = row_token;
+  a.token_rows = token_rows;
+  a.work = static_cast<int32_t*>(workspace);
+  return launched(dsfp8::launch_route(a, stream));
+}
+
+dsfp8_status dsfp8_moe_combine(const void* yr, int64_t R, int64_t ldy, const int32_t* indices, int64_t ldi,
+                               const void* weights, int64_t ldw, const int32_t* token_rows, int64_t T, int64_t k,
+                               int64_t D, void* out, int64_t ldo, hipStream_t stream) {
+  if (!dim_ok(R) || !dim_ok(T) || !dim_ok(D) || k < 1 || k > 16) return DSFP8_ERR_SHAPE;
+  DSFP8_TRY(check_mat(yr, R, D, ldy, 2));
+  DSFP8_TRY(check_mat(indices, T, k, ldi, 4));
+  DSFP8_TRY(check_mat(weights, T, k, ldw, 2));
+  DSFP8_TRY(check_mat(token_rows, T, k, k, 4));
+  DSFP8_TRY(check_mat(out, T, D, ldo, 2));
+  dsfp8::CombineArgs a{};
+  a.yr = static_cast<const uint16_t*>(yr);
+  a.ldy = ldy;
+  a.R = R;
+  a.indices = indices;
+  a.ldi = ldi;
+  a.weights = static_cast<const uint16_t*>(weights);
+  a.ldw = ldw;
+  a.token_rows = token_rows;
+  a.T = T;
+  a.k = k;
+  a.D = D;
+  a.out = static_cast<uint16_t*>(out);
+  a.ldo = ldo;
+  return launched(dsfp8::launch_combine(a, stream));
+}
+
 }  // extern "C"

@@ -21,6 +21,39 @@ struct ActQuantArgs {
   uint16_t* h;        // optional bf16 output of SiLU(g)*u
   int64_t ldh;
   bool ue8m0;
+  // optional row gather (plain act_quant only): output row m quantises input
+  // row rows[m], clamped to [0, g_rows)
+  const int32_t* rows;
+  int64_t g_rows;
+};
+
+// Routing of T*k (token, slot) pairs to experts (stable counting sort).
+constexpr int kRouteChunk = 512;  // pairs per chunk
+constexpr int kMaxRouteExperts = 8192;
+struct RouteArgs {
+  const int32_t* indices;  // [T, k], row stride ldi
+  int64_t ldi, k, n;       // n = T * k
+  int E;
+  int32_t* offsets;        // [E + 1]
+  int32_t* row_token;      // [n]
+  int32_t* token_rows;     // [T, k] contiguous
+  int32_t* work;           // [chunks, E]
+  int64_t chunks;
+};
+
+// Weighted combine of the expert outputs per token.
+struct CombineArgs {
+  const uint16_t* yr;  // bf16 [R, D], row stride ldy
+  int64_t ldy, R;
+  const int32_t* indices;     // [T, k], row stride ldi
+  int64_t ldi;
+  const uint16_t* weights;    // bf16 [T, k], row stride ldw
+  int64_t ldw;
+  const int32_t* token_rows;  // [T, k] contiguous
+  int64_t T, k, D;
+  uint16_t* out;              // bf16 [T, D], row stride ldo
+  int64_t ldo;
+  bool vec;
 };
 
 struct WeightQuantArgs {
@@ -66,6 +99,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream);
+hipError_t launch_route(RouteArgs a, hipStream_t stream);
+size_t route_workspace_bytes(int64_t n, int64_t E);
+hipError_t launch_combine(CombineArgs a, hipStream_t stream);
 hipError_t launch_weight_quant(const WeightQuantArgs& a, hipStream_t stream);
 hipError_t launch_weight_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);

@@ -138,7 +138,12 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(ActQuantArgs a, int
       ms[i] = m;
       bs[i] = b;
       const int64_t col = b * kBlock + lane16 * 8;
-      wg[i] = load8<VEC>(a.g, a.ldg, m, col, a.K, live[i]);
+      int64_t msrc = m;
+      if (!FUSED && a.rows != nullptr && live[i]) {
+        msrc = a.rows[m];
+        msrc = msrc < 0 ? 0 : (msrc >= a.g_rows ? a.g_rows - 1 : msrc);
+      }
+      wg[i] = load8<VEC>(a.g, a.ldg, msrc, col, a.K, live[i]);
       if (FUSED) wu[i] = load8<VEC>(a.u, a.ldu, m, col, a.K, live[i]);
     }
 #pragma unroll

@@ -239,6 +239,68 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda,
 
 size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K);
 
+/*
+ * act_quant of gathered rows: the expert inputs x[idx] of [AG] 6.4 / 8.4
+ * quantised without writing the gathered bf16 copy:
+ *   y[m], s[m] = act_quant(x[rows[m]])   for 0 <= m < M.
+ *
+ *   x      bf16 [x_rows, K], row stride ldx                  (device, read)
+ *   rows   int32 [M]; each entry is clamped to [0, x_rows)  (device, read)
+ *   y, s   e4m3 [M, K] and fp32 scales, as for dsfp8_act_quant (device, written)
+ * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, LAUNCH.
+ */
+dsfp8_status dsfp8_act_quant_rows(const void* x, int64_t x_rows, int64_t ldx, const int32_t* rows,
+                                  int64_t M, int64_t K, void* y, int64_t ldy,
+                                  float* s, int64_t s_row_stride, int64_t s_kb_stride,
+                                  int scale_fmt, hipStream_t stream);
+
+/*
+ * Routing for the grouped product ([AG] 6.4 / 8.4: for each expert i in
+ * increasing order, the (idx, top) pairs with indices == i, in the order
+ * torch.where lists them).  The T*k (token, slot) pairs are sorted stably by
+ * expert: rows offsets[e] .. offsets[e+1]-1 are expert e's pairs in increasing
+ * t*k + j.  Deterministic (no atomics on global memory).
+ *
+ *   indices     int32 [T, k], row stride ldi: expert of each (token, slot)
+ *                                                           (device, read)
+ *   offsets     int32 [E+1]; offsets[E] = number of routed pairs
+ *                                                           (device, written)
+ *   row_token   int32 [T*k]: token of each row; entries at or past
+ *               offsets[E] are left untouched               (device, written)
+ *   token_rows  int32 [T, k] contiguous: row of each pair; -1 for a pair whose
+ *               index is outside [0, E) (it gets no row)    (device, written)
+ *   workspace   at least dsfp8_moe_route_workspace_bytes(T, k, E) bytes,
+ *               4-byte aligned                              (device, scratch)
+ * Limits: 1 <= k <= 16, 1 <= E <= 8192, T*k < 2^31.
+ * Errors: NULL, SHAPE, LD, ALIGN, WORKSPACE, LAUNCH.
+ */
+dsfp8_status dsfp8_moe_route(const int32_t* indices, int64_t T, int64_t k, int64_t ldi, int64_t E,
+                             int32_t* offsets, int32_t* row_token, int32_t* token_rows,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t dsfp8_moe_route_workspace_bytes(int64_t T, int64_t k, int64_t E);
+
+/*
+ * Weighted combine of the expert outputs ([AG] 6.4 / 8.4:
+ * y[idx] += expert(x[idx]) * weights[idx, top] for each expert in increasing
+ * order, y starting at zero, in bf16):
+ *   out[t] = the sum over the token's pairs, taken in increasing expert index,
+ *            of bf16(yr[token_rows[t, j]] * weights[t, j]), each addition
+ *            rounded to bf16 (round-to-nearest-even).
+ *
+ *   yr          bf16 [R, D], row stride ldy: expert outputs by row (device, read)
+ *   indices     int32 [T, k], row stride ldi                       (device, read)
+ *   weights     bf16 [T, k], row stride ldw                        (device, read)
+ *   token_rows  int32 [T, k] contiguous, from dsfp8_moe_route; entries
+ *               outside [0, R) are skipped                         (device, read)
+ *   out         bf16 [T, D], row stride ldo                        (device, written)
+ * Limits: 1 <= k <= 16.  Errors: NULL, SHAPE, LD, ALIGN, LAUNCH.
+ */
+dsfp8_status dsfp8_moe_combine(const void* yr, int64_t R, int64_t ldy,
+                               const int32_t* indices, int64_t ldi, const void* weights, int64_t ldw,
+                               const int32_t* token_rows, int64_t T, int64_t k, int64_t D,
+                               void* out, int64_t ldo, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,3 +160,37 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
         _lib.load()
+
+
+def test_routed_expert_validation(lib):
+    # dsfp8_moe_route(indices, T, k, ldi, E, offsets, row_token, token_rows, ws, wsb, stream)
+    r = lib.dsfp8_moe_route
+    need = lib.dsfp8_moe_route_workspace_bytes(4096, 8, 256)
+    assert need == 64 * 256 * 4
+    assert lib.dsfp8_moe_route_workspace_bytes(4096, 17, 256) == 0
+    assert lib.dsfp8_moe_route_workspace_bytes(4096, 8, 9000) == 0
+    assert r(P, 4096, 0, 8, 256, P, P, P, P, need, None) == SHAPE
+    assert r(P, 4096, 17, 17, 256, P, P, P, P, need, None) == SHAPE
+    assert r(P, 4096, 8, 8, 0, P, P, P, P, need, None) == SHAPE
+    assert r(P, 4096, 8, 8, 8193, P, P, P, P, need, None) == SHAPE
+    assert r(P, 4096, 8, 7, 256, P, P, P, P, need, None) == LD
+    assert r(None, 4096, 8, 8, 256, P, P, P, P, need, None) == NULL
+    assert r(P, 4096, 8, 8, 256, None, P, P, P, need, None) == NULL
+    assert r(P, 4096, 8, 8, 256, P, P, P + 2, P, need, None) == ALIGN
+    assert r(P, 4096, 8, 8, 256, P, P, P, P, need - 1, None) == WS
+    assert r(P, 4096, 8, 8, 256, P, P, P, None, need, None) == NULL
+    # dsfp8_moe_combine(yr, R, ldy, indices, ldi, weights, ldw, token_rows, T, k, D, out, ldo, stream)
+    c = lib.dsfp8_moe_combine
+    assert c(P, 64, 256, P, 8, P, 8, P, 8, 0, 256, P, 256, None) == SHAPE
+    assert c(P, 64, 256, P, 8, P, 8, P, 8, 17, 256, P, 256, None) == SHAPE
+    assert c(P, 64, 255, P, 8, P, 8, P, 8, 8, 256, P, 256, None) == LD
+    assert c(P, 64, 256, P, 8, P, 7, P, 8, 8, 256, P, 256, None) == LD
+    assert c(P, 64, 256, P, 8, P, 8, P, 8, 8, 256, P + 1, 256, None) == ALIGN
+    assert c(P, 64, 256, None, 8, P, 8, P, 8, 8, 256, P, 256, None) == NULL
+    # dsfp8_act_quant_rows(x, x_rows, ldx, rows, M, K, y, ldy, s, srs, sks, fmt, stream)
+    q = lib.dsfp8_act_quant_rows
+    assert q(P, 0, 256, P, 4, 256, P, 256, P, 1, 4, 0, None) == SHAPE
+    assert q(P, 8, 256, None, 4, 256, P, 256, P, 1, 4, 0, None) == NULL
+    assert q(P, 8, 256, P + 2, 4, 256, P, 256, P, 1, 4, 0, None) == ALIGN
+    assert q(P, 8, 256, P, 4, 256, P, 256, P, 1, 4, 7, None) == FMT
+    assert q(P, 8, 255, P, 4, 256, P, 256, P, 1, 4, 0, None) == LD

@@ -15,6 +15,7 @@ import torch
 import block_scaled_fp8_act_amd as ds
 from block_scaled_fp8_act_amd import inputs as I
 from oracle import gemm as G
+from oracle import moe
 from oracle import quant as Q
 
 from gpu_helpers import check_product, dev_f32, dev_scales, dev_u8, host_bits16, host_u8
@@ -98,7 +99,10 @@ def test_routed_experts_full_size_sampled(proj):
     dims = I.WORKLOADS["moe"].dims
     E, dim, inter = dims["experts"], dims["dim"], dims["inter"]
     N, K = (2 * inter, dim) if proj == "up" else (dim, inter)
-    tok, off, counts = I.zipf_routing(dims["tokens"], E, dims["topk"], dims["zipf_s"])
+    idx, _ = I.zipf_topk(dims["tokens"], E, dims["topk"], dims["zipf_s"])
+    off, tok, _, _ = moe.route(idx, E)
+    off = off.astype(np.int32)
+    counts = np.diff(off)
     M = int(off[-1])
     # activations: the routed rows (token gathered per row), drawn on the device
     xt = I.device_normal((dims["tokens"], K), seed=900, std=1.0, device="cuda", dtype=torch.bfloat16)
