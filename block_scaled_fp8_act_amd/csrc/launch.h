@@ -28,8 +28,9 @@ struct ActQuantArgs {
 };
 
 // Routing of T*k (token, slot) pairs to experts (stable counting sort).
-constexpr int kRouteChunk = 512;  // pairs per chunk
-constexpr int kMaxRouteExperts = 8192;
+constexpr int kRouteChunk = 512;      // least pairs per chunk
+constexpr int kMaxRouteChunks = 64;   // most chunks
+constexpr int kMaxRouteExperts = 4096;
 struct RouteArgs {
   const int32_t* indices;  // [T, k], row stride ldi
   int64_t ldi, k, n;       // n = T * k
@@ -37,8 +38,8 @@ struct RouteArgs {
   int32_t* offsets;        // [E + 1]
   int32_t* row_token;      // [n]
   int32_t* token_rows;     // [T, k] contiguous
-  int32_t* work;           // [chunks, E]
-  int64_t chunks;
+  int32_t* work;           // [E, chunks]
+  int64_t chunk, chunks;   // pairs per chunk, number of chunks
 };
 
 // Weighted combine of the expert outputs per token.

@@ -3,18 +3,23 @@
 // increasing order, the (token, slot) pairs that chose it run through the
 // expert, and each token's output accumulates weight * expert output).
 //
-// Routing: a stable counting sort of the T*k pairs by expert.  The rows of
+// Routing: a stable counting sort of the T*k pairs by expert (T*k < 2^31, so
+// pair indices are divided by k in 32 bits).  The rows of
 // expert e are its pairs in increasing pair index t*k + j (the order in which
-// torch.where lists them).  Three kernels, none with global atomics, so the
+// torch.where lists them).  Two kernels, no atomics on global memory, so the
 // result is deterministic:
-//   count   -- one workgroup per chunk of kRouteChunk pairs, per-expert counts
-//              in LDS;
-//   scan    -- one workgroup: exclusive prefix over (expert, chunk) in
-//              expert-major order, giving every chunk's first row per expert
-//              and the expert offsets;
-//   scatter -- one wavefront per chunk, 64 pairs at a time: a lane's row is
-//              the chunk's running count of its expert plus the number of
-//              lower lanes with the same expert.
+//   count   -- one workgroup per chunk of pairs, per-expert counts in LDS,
+//              stored expert-major (counts[e][c]);
+//   scatter -- one workgroup per chunk.  All its threads first reduce the
+//              (small) count table: expert totals, an exclusive scan of them
+//              for the expert offsets, and the counts of earlier chunks, so
+//              the chunk's first row for each expert is known.  Then one
+//              wavefront walks the chunk 64 pairs at a time: a lane's row is
+//              the running count of its expert plus the number of lower lanes
+//              with the same expert (found with ballots over the bits of the
+//              expert index).
+// The chunk size grows with the number of pairs so that there are at most
+// kMaxRouteChunks chunks and the table stays small.
 //
 // Combine: one token per workgroup row, 8 columns per lane; the token's
 // contributions are taken in increasing expert order, each weighted product
@@ -32,90 +37,123 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- routing -----------------------------------------------------------------------
 
-__global__ __launch_bounds__(64) void route_count_kernel(RouteArgs a) {
+constexpr int kRouteExpertBits = 12;  // experts below 2^12
+static_assert(kMaxRouteExperts <= (1 << kRouteExpertBits), "expert bits");
+constexpr int kRouteThreads = 256;
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a) {
   extern __shared__ int32_t cnt[];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < a.E; e += 64) cnt[e] = 0;
+  const int t = threadIdx.x;
+  for (int e = t; e < a.E; e += kRouteThreads) cnt[e] = 0;
   __syncthreads();
-  const int64_t p0 = (int64_t)blockIdx.x * kRouteChunk;
-  for (int i = lane; i < kRouteChunk; i += 64) {
-    const int64_t p = p0 + i;
-    if (p >= a.n) break;
-    const int32_t e = a.indices[(p / a.k) * a.ldi + p % a.k];
+  const int64_t p0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t p1 = p0 + a.chunk < a.n ? p0 + a.chunk : a.n;
+  for (int64_t p = p0 + t; p < p1; p += kRouteThreads) {
+    const int32_t e = a.indices[(int64_t)((uint32_t)p / (uint32_t)a.k) * a.ldi + (uint32_t)p % (uint32_t)a.k];
     if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  for (int e = lane; e < a.E; e += 64) a.work[(int64_t)blockIdx.x * a.E + e] = cnt[e];
+  for (int e = t; e < a.E; e += kRouteThreads) a.work[(int64_t)e * a.chunks + blockIdx.x] = cnt[e];
 }
 
-// Exclusive prefix over q = e * chunks + c (expert-major) of work[c * E + e],
-// written back in place; offsets[e] = first row of expert e, offsets[E] = the
-// number of routed pairs.  Each thread scans a contiguous range of q.
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a) {
-  __shared__ int64_t part[kScanThreads];
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a) {
+  extern __shared__ int32_t lds[];
+  int32_t* next = lds;                       // [E]: next row of each expert
+  int32_t* total = lds + a.E;                // [E]: pairs of each expert
+  __shared__ int32_t wsum[kRouteThreads];
   const int t = threadIdx.x;
-  if (a.chunks == 0) {  // no pairs: every expert is empty
-    for (int e = t; e <= a.E; e += kScanThreads) a.offsets[e] = 0;
-    return;
-  }
-  const int64_t Q = a.chunks * a.E;
-  const int64_t per = (Q + kScanThreads - 1) / kScanThreads;
-  const int64_t q0 = t * per, q1 = q0 + per < Q ? q0 + per : Q;
-  auto at = [&](int64_t q) -> int32_t& {
-    const int64_t e = q / a.chunks, c = q % a.chunks;
-    return a.work[c * a.E + e];
-  };
-  int64_t sum = 0;
-  for (int64_t q = q0; q < q1; ++q) sum += at(q);
-  part[t] = sum;
-  __syncthreads();
-  // Inclusive scan of the per-thread sums (Hillis-Steele over LDS).
-  for (int d = 1; d < kScanThreads; d <<= 1) {
-    const int64_t v = t >= d ? part[t - d] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  int64_t run = t > 0 ? part[t - 1] : 0;
-  for (int64_t q = q0; q < q1; ++q) {
-    int32_t& w = at(q);
-    const int32_t c = w;
-    if (q % a.chunks == 0) a.offsets[q / a.chunks] = (int32_t)run;
-    w = (int32_t)run;
-    run += c;
-  }
-  if (t == kScanThreads - 1) a.offsets[a.E] = (int32_t)part[kScanThreads - 1];
-}
-
-__global__ __launch_bounds__(64) void route_scatter_kernel(RouteArgs a) {
-  extern __shared__ int32_t next[];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < a.E; e += 64) next[e] = a.work[(int64_t)blockIdx.x * a.E + e];
-  __syncthreads();
-  const int64_t p0 = (int64_t)blockIdx.x * kRouteChunk;
-  for (int r = 0; r < kRouteChunk / 64; ++r) {
-    const int64_t p = p0 + r * 64 + lane;
-    const bool in = p < a.n;
-    const int64_t t = in ? p / a.k : 0;
-    const int32_t e = in ? a.indices[t * a.ldi + p % a.k] : -1;
-    const bool valid = e >= 0 && e < a.E;
-    int rank = 0, later = 0;
+  const int c = blockIdx.x;
+  // Per expert: the total over all chunks and the part in chunks before this
+  // one.  A row of the table (at most kMaxRouteChunks entries) is loaded at
+  // once.  A thread's experts are contiguous, so the exclusive scan of the
+  // totals is a per-thread sum plus a block scan.
+  const int per = (a.E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = t * per < a.E ? t * per : a.E;
+  const int e1 = e0 + per < a.E ? e0 + per : a.E;
+  int32_t tsum = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int32_t* row = a.work + (int64_t)e * a.chunks;
+    int32_t v[kMaxRouteChunks];
 #pragma unroll
-    for (int l = 0; l < 64; ++l) {
-      const int32_t el = __builtin_amdgcn_readlane(e, l);
-      rank += (el == e && l < lane) ? 1 : 0;
-      later += (el == e && l > lane) ? 1 : 0;
+    for (int j = 0; j < kMaxRouteChunks; ++j) v[j] = j < a.chunks ? row[j] : 0;
+    int32_t tot = 0, before = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRouteChunks; ++j) {
+      tot += v[j];
+      before += j < c ? v[j] : 0;
     }
-    // Every lane reads its expert's running count before the last lane of
-    // each expert advances it (LDS operations of one wavefront complete in
-    // order).
-    const int32_t pos = valid ? next[e] + rank : -1;
-    if (valid) a.row_token[pos] = (int32_t)t;
-    if (in) a.token_rows[p] = pos;
-    if (valid && later == 0) next[e] = pos + 1;
-    __builtin_amdgcn_wave_barrier();
+    next[e] = before;
+    total[e] = tot;
+    tsum += tot;
+  }
+  wsum[t] = tsum;
+  __syncthreads();
+  for (int d = 1; d < kRouteThreads; d <<= 1) {
+    const int32_t v = t >= d ? wsum[t - d] : 0;
+    __syncthreads();
+    wsum[t] += v;
+    __syncthreads();
+  }
+  // Expert e's first row is the scanned total of the experts before it.
+  int32_t run = t > 0 ? wsum[t - 1] : 0;
+  for (int e = e0; e < e1; ++e) {
+    if (c == 0) a.offsets[e] = run;
+    next[e] += run;
+    run += total[e];
+  }
+  if (c == 0 && t == kRouteThreads - 1) a.offsets[a.E] = wsum[kRouteThreads - 1];
+  __syncthreads();
+  if (t >= 64) return;
+
+  // One wavefront assigns the chunk's rows, 64 pairs per round; the indices
+  // of kBatch rounds are loaded together.
+  const int lane = t;
+  const int64_t p0 = (int64_t)c * a.chunk;
+  const int64_t p1 = p0 + a.chunk < a.n ? p0 + a.chunk : a.n;
+  constexpr int kBatch = 8;
+  for (int64_t pbb = p0; pbb < p1; pbb += 64 * kBatch) {
+    int32_t ev[kBatch];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int64_t p = pbb + r * 64 + lane;
+      ev[r] = p < p1 ? a.indices[(int64_t)((uint32_t)p / (uint32_t)a.k) * a.ldi + (uint32_t)p % (uint32_t)a.k] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int64_t p = pbb + r * 64 + lane;
+      const bool in = p < p1;
+      const int32_t e = ev[r];
+      const bool valid = e >= 0 && e < a.E;
+      // Lanes with the same expert: intersect, over the expert's bits and a
+      // validity bit, the ballot of lanes agreeing with this lane on that bit.
+      uint64_t same = ~0ull;
+      {
+        const uint64_t vb = __ballot(valid);
+        same &= valid ? vb : ~vb;
+      }
+#pragma unroll
+      for (int b = 0; b < kRouteExpertBits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        same &= bit ? bb : ~bb;
+      }
+      const int rank =
+          (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
+      const int later = __popcll(same) - rank - 1;
+      // Every lane reads its expert's running count before the last lane of
+      // each expert advances it (LDS operations of one wavefront complete in
+      // order).
+      const int32_t pos = valid ? next[e] + rank : -1;
+      if (valid) a.row_token[pos] = (int32_t)((uint32_t)p / (uint32_t)a.k);
+      if (in) a.token_rows[p] = pos;
+      if (valid && later == 0) next[e] = pos + 1;
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
@@ -195,23 +233,32 @@ inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_
 
 }  // namespace
 
+// Chunk size: at least kRouteChunk pairs, at most kMaxRouteChunks chunks.
+static int64_t route_chunk(int64_t n) {
+  int64_t c = (n + kMaxRouteChunks - 1) / kMaxRouteChunks;
+  c = (c + 63) / 64 * 64;
+  return c > kRouteChunk ? c : kRouteChunk;
+}
+
 size_t route_workspace_bytes(int64_t n, int64_t E) {
-  const int64_t chunks = (n + kRouteChunk - 1) / kRouteChunk;
+  const int64_t chunk = route_chunk(n);
+  const int64_t chunks = (n + chunk - 1) / chunk;
   return (size_t)(chunks > 0 ? chunks : 1) * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_route(RouteArgs a, hipStream_t stream) {
-  a.chunks = (a.n + kRouteChunk - 1) / kRouteChunk;
-  const size_t lds = (size_t)a.E * sizeof(int32_t);
-  if (a.chunks > 0) {
-    hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)a.chunks), dim3(64), lds, stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  a.chunk = route_chunk(a.n);
+  a.chunks = (a.n + a.chunk - 1) / a.chunk;
+  const size_t lds = (size_t)a.E * sizeof(int32_t);  // count; the scatter uses twice this
+  if (a.chunks == 0) {  // no pairs: every expert is empty
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((a.E + 1 + 255) / 256)), dim3(256), 0, stream, a.offsets,
+                       (int64_t)a.E + 1, 0);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
+  hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)a.chunks), dim3(kRouteThreads), lds, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.chunks == 0) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)a.chunks), dim3(64), lds, stream, a);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)a.chunks), dim3(kRouteThreads), 2 * lds, stream, a);
   return hipGetLastError();
 }
 

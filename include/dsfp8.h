@@ -271,7 +271,7 @@ dsfp8_status dsfp8_act_quant_rows(const void* x, int64_t x_rows, int64_t ldx, co
  *               index is outside [0, E) (it gets no row)    (device, written)
  *   workspace   at least dsfp8_moe_route_workspace_bytes(T, k, E) bytes,
  *               4-byte aligned                              (device, scratch)
- * Limits: 1 <= k <= 16, 1 <= E <= 8192, T*k < 2^31.
+ * Limits: 1 <= k <= 16, 1 <= E <= 4096, T*k < 2^31.
  * Errors: NULL, SHAPE, LD, ALIGN, WORKSPACE, LAUNCH.
  */
 dsfp8_status dsfp8_moe_route(const int32_t* indices, int64_t T, int64_t k, int64_t ldi, int64_t E,

@@ -166,13 +166,13 @@ def test_routed_expert_validation(lib):
     # dsfp8_moe_route(indices, T, k, ldi, E, offsets, row_token, token_rows, ws, wsb, stream)
     r = lib.dsfp8_moe_route
     need = lib.dsfp8_moe_route_workspace_bytes(4096, 8, 256)
-    assert need == 64 * 256 * 4
+    assert need == 64 * 256 * 4  # 32768 pairs in 64 chunks of 512
     assert lib.dsfp8_moe_route_workspace_bytes(4096, 17, 256) == 0
-    assert lib.dsfp8_moe_route_workspace_bytes(4096, 8, 9000) == 0
+    assert lib.dsfp8_moe_route_workspace_bytes(4096, 8, 4097) == 0
     assert r(P, 4096, 0, 8, 256, P, P, P, P, need, None) == SHAPE
     assert r(P, 4096, 17, 17, 256, P, P, P, P, need, None) == SHAPE
     assert r(P, 4096, 8, 8, 0, P, P, P, P, need, None) == SHAPE
-    assert r(P, 4096, 8, 8, 8193, P, P, P, P, need, None) == SHAPE
+    assert r(P, 4096, 8, 8, 4097, P, P, P, P, need, None) == SHAPE
     assert r(P, 4096, 8, 7, 256, P, P, P, P, need, None) == LD
     assert r(None, 4096, 8, 8, 256, P, P, P, P, need, None) == NULL
     assert r(P, 4096, 8, 8, 256, None, P, P, P, need, None) == NULL
