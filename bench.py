@@ -5,15 +5,18 @@ Headline workload: the dense FFN at prefill (4096 tokens, dim 7168, inter
 already resident in HBM:
 
     act_quant(x [4096, 7168])                          -> e4m3 + scales
-    gemm(x_q, [w1; w3] e4m3 [36864, 7168])             -> bf16 [4096, 36864]
-    silu_mul_act_quant(h1, h3)                         -> e4m3 [4096, 18432] + scales
+    gemm_silu_mul_act_quant(x_q, [w1; w3] e4m3 [36864, 7168])
+                                                       -> e4m3 [4096, 18432] + scales
+        (the up-projection with the SiLU gate and the next act_quant in
+        its epilogue)
     gemm(h_q, w2 e4m3 [7168, 18432])                   -> bf16 [4096, 7168]
 
 ``value`` is the step's GEMM work (3 x 2*4096*18432*7168 flop) divided by the
 step time, in TFLOP/s.  Every kernel launch is bracketed by HIP events on the
 launch stream, which gives each kernel's average duration; ``roofline``
-reports the dominant kernel (the up-projection GEMM) against the FP8 dense
-MFMA peak.  The other workloads (routed experts, weight dequantisation, the
+reports the dominant kernel (the gated up-projection) against the FP8 dense
+MFMA peak.  The same step with the product, gate and quantisation as
+separate kernels is reported under ``other_workloads`` for comparison.  The other workloads (routed experts, weight dequantisation, the
 decode projection, the ragged ue8m0 case) are timed the same way and reported
 under ``other_workloads``.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same step.
@@ -78,7 +81,7 @@ class Timer:
 
 # ---- dense FFN step ---------------------------------------------------------------------
 
-def setup_dense(dev, fmt="fp32"):
+def setup_dense(dev, fmt="fp32", unfused=False):
     d = I.WORKLOADS["dense_ffn"].dims
     M, D, F = d["M"], d["dim"], d["inter"]
     x = I.device_normal((M, D), seed=301, std=1.0, device=dev, dtype=torch.bfloat16)
@@ -92,21 +95,25 @@ def setup_dense(dev, fmt="fp32"):
         x=x, q13=q13, s13=s13, q2=q2, s2=s2,
         xq=torch.empty((M, D), dtype=torch.uint8, device=dev),
         xs=ds.new_scales(M, kb(D), dev),
-        h13=torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev),
+        h13=torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev) if unfused else None,
         hq=torch.empty((M, F), dtype=torch.uint8, device=dev),
         hs=ds.new_scales(M, kb(F), dev),
         out=torch.empty((M, D), dtype=torch.bfloat16, device=dev),
     )
     torch.cuda.synchronize()
-    return dict(M=M, D=D, F=F, b=bufs, fmt=fmt)
+    return dict(M=M, D=D, F=F, b=bufs, fmt=fmt, unfused=unfused)
 
 
 def dense_step(st, T):
     b, F, fmt = st["b"], st["F"], st["fmt"]
     T.run("act_quant", lambda: ds.act_quant(b["x"], fmt, out=(b["xq"], b["xs"])))
-    T.run("gemm_up", lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"], scale_fmt=fmt))
-    T.run("silu_mul_act_quant",
-          lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:], fmt, out=(b["hq"], b["hs"])))
+    if st["unfused"]:
+        T.run("gemm_up", lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"], scale_fmt=fmt))
+        T.run("silu_mul_act_quant",
+              lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:], fmt, out=(b["hq"], b["hs"])))
+    else:
+        T.run("gemm_up_gate",
+              lambda: ds.gemm_silu_mul_act_quant(b["xq"], b["xs"], b["q13"], b["s13"], fmt, out=(b["hq"], b["hs"])))
     T.run("gemm_down", lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"], scale_fmt=fmt))
 
 
@@ -132,12 +139,16 @@ def run_dense(st, steps, warmup):
 def dense_kernels(st, T):
     M, D, F = st["M"], st["D"], st["F"]
     k = {}
-    for name, fl in (("gemm_up", 2.0 * M * 2 * F * D), ("gemm_down", 2.0 * M * D * F)):
+    up = "gemm_up" if st["unfused"] else "gemm_up_gate"
+    for name, fl in ((up, 2.0 * M * 2 * F * D), ("gemm_down", 2.0 * M * D * F)):
         us = T.avg_us(name)
-        k[name] = {"shape": [M, 2 * F if name == "gemm_up" else D, D if name == "gemm_up" else F],
+        k[name] = {"shape": [M, 2 * F if name == up else D, D if name == up else F],
                    "us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
                    "frac_of_fp8_peak": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
-    for name, by in (("act_quant", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2))):
+    mem = [("act_quant", aq_bytes(M, D))]
+    if st["unfused"]:
+        mem.append(("silu_mul_act_quant", aq_bytes(M, F, 2)))
+    for name, by in mem:
         us = T.avg_us(name)
         k[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                    "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}
@@ -149,7 +160,7 @@ def bench_bf16_path(dev, steps):
     comparison: each linear dequantises its e4m3 weight with weight_dequant
     and multiplies in bf16 (the vendor library's GEMM through
     torch.mm, a two-dimensional product); the gate is SiLU(w1 x) * (w3 x) in bf16."""
-    st = setup_dense(dev)
+    st = setup_dense(dev, unfused=True)
     b, M, D, F = st["b"], st["M"], st["D"], st["F"]
     w13 = torch.empty((2 * F, D), dtype=torch.bfloat16, device=dev)
     w2 = torch.empty((D, F), dtype=torch.bfloat16, device=dev)
@@ -198,6 +209,19 @@ def bench_dense_ue8m0(dev, steps):
             "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "kernels": dense_kernels(st, T)}
 
 
+def bench_dense_unfused(dev, steps):
+    """The dense step with the product, the SiLU gate and the quantisation of
+    h as three kernels (bf16 [4096, 36864] written and read back between
+    them), for comparison with the gated product."""
+    st = setup_dense(dev, unfused=True)
+    ms, T = run_dense(st, steps, 3)
+    M, D, F = st["M"], st["D"], st["F"]
+    flop = 2.0 * M * 2 * F * D + 2.0 * M * D * F
+    return {"workload": "dense FFN prefill, up-projection, gate and quantisation as separate kernels",
+            "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+            "kernels": dense_kernels(st, T)}
+
+
 def gemm_bytes(M, N, K):
     return M * K + N * K + 4 * (M * kb(K) + kb(N) * kb(K)) + 2 * M * N
 
@@ -211,8 +235,8 @@ def aq_bytes(M, K, inputs=1):
 def bench_moe(dev, iters):
     """The routed-expert step on the device: routing of the gate's top-k
     choice, act_quant of the routed rows (gathered in the kernel), the grouped
-    [w1;w3] product, the fused SiLU gate and act_quant, the grouped w2 product
-    and the weighted bf16 combine into the token outputs."""
+    [w1;w3] product with the SiLU gate and act_quant in its epilogue, the
+    grouped w2 product and the weighted bf16 combine into the token outputs."""
     d = I.WORKLOADS["moe"].dims
     E, D, F, Tk, k = d["experts"], d["dim"], d["inter"], d["tokens"], d["topk"]
     idx_h, w_h = I.zipf_topk(Tk, E, k, d["zipf_s"])
@@ -242,7 +266,6 @@ def bench_moe(dev, iters):
     rws = torch.empty(lib.dsfp8_moe_route_workspace_bytes(Tk, k, E), dtype=torch.uint8, device=dev)
     xq = torch.empty((M, D), dtype=torch.uint8, device=dev)
     xs = ds.new_scales(M, kb(D), dev)
-    h13 = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
     hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
     hs = ds.new_scales(M, kb(F), dev)
     yr = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
@@ -259,8 +282,8 @@ def bench_moe(dev, iters):
     def step():
         T.run("route", route)
         T.run("act_quant_rows", lambda: ds.act_quant_rows(x, row_token, out=(xq, xs)))
-        T.run("grouped_up", lambda: ds.grouped_gemm(xq, xs, q13, s13, offd, out=h13, workspace=ws))
-        T.run("silu_mul_act_quant", lambda: ds.silu_mul_act_quant(h13[:, :F], h13[:, F:], out=(hq, hs)))
+        T.run("grouped_up_gate",
+              lambda: ds.grouped_gemm_silu_mul_act_quant(xq, xs, q13, s13, offd, out=(hq, hs), workspace=ws))
         T.run("grouped_down", lambda: ds.grouped_gemm(hq, hs, q2, s2, offd, out=yr, workspace=ws))
         T.run("combine", lambda: ds.moe_combine(yr, idx, wts, token_rows, out=y))
 
@@ -278,20 +301,19 @@ def bench_moe(dev, iters):
     T.collect()
     torch.cuda.synchronize()
     flop_up, flop_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
-    by_up = M * D + E * 2 * F * D + 4 * (M * kb(D) + E * kb(2 * F) * kb(D)) + 2 * M * 2 * F
+    by_up = M * D + E * 2 * F * D + 4 * (M * kb(D) + E * kb(2 * F) * kb(D)) + M * F + 4 * M * kb(F)
     by_dn = M * F + E * D * F + 4 * (M * kb(F) + E * kb(D) * kb(F)) + 2 * M * D
     res = {"workload": I.WORKLOADS["moe"].desc, "rows": M,
            "expert_rows": {"min": int(counts.min()), "median": float(np.median(counts)),
                            "max": int(counts.max())}}
-    for name, fl, by in (("grouped_up", flop_up, by_up), ("grouped_down", flop_dn, by_dn)):
+    for name, fl, by in (("grouped_up_gate", flop_up, by_up), ("grouped_down", flop_dn, by_dn)):
         us = T.avg_us(name)
         roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
         res[name] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
                      "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3)}
     # act_quant_rows reads the routed rows of x (2 B), writes e4m3 and scales;
     # combine reads the expert outputs and writes the token outputs (bf16).
-    for name, by in (("act_quant_rows", aq_bytes(M, D)), ("silu_mul_act_quant", aq_bytes(M, F, 2)),
-                     ("combine", 2 * M * D + 2 * Tk * D + Tk * k * 10)):
+    for name, by in (("act_quant_rows", aq_bytes(M, D)), ("combine", 2 * M * D + 2 * Tk * D + Tk * k * 10)):
         us = T.avg_us(name)
         res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                      "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
@@ -425,9 +447,9 @@ def gemm_source_digest():
 
 
 def recorded_traffic():
-    """HBM bytes per launch of the up-projection GEMM, from the counter summary
+    """HBM bytes per launch of the gated up-projection, from the counter summary
     in profiles/, or None if it was taken on a different GEMM source."""
-    path = os.path.join(ROOT, "profiles", "gemm_dense_ffn_up_counters.md")
+    path = os.path.join(ROOT, "profiles", "gemm_dense_ffn_up_gate_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -442,6 +464,9 @@ def recorded_traffic():
 
 def only(kernel, reps, dev):
     """Run one kernel of the dense step `reps` times (for counter collection)."""
+    if kernel == "routed_experts":
+        print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps)}))
+        return
     if kernel == "copy":
         # calibration: a plain 1 GiB device-to-device copy (1 GiB read, 1 GiB written)
         src = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
@@ -450,11 +475,13 @@ def only(kernel, reps, dev):
         for _ in range(reps):
             dst.copy_(src)
     else:
-        st = setup_dense(dev)
+        st = setup_dense(dev, unfused=kernel in ("gemm_up", "silu_mul_act_quant"))
         T = Timer()
         b, F = st["b"], st["F"]
         fns = {
             "act_quant": lambda: ds.act_quant(b["x"], out=(b["xq"], b["xs"])),
+            "gemm_up_gate": lambda: ds.gemm_silu_mul_act_quant(b["xq"], b["xs"], b["q13"], b["s13"],
+                                                               out=(b["hq"], b["hs"])),
             "gemm_up": lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"]),
             "silu_mul_act_quant": lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:],
                                                                 out=(b["hq"], b["hs"])),
@@ -475,8 +502,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["act_quant", "gemm_up", "silu_mul_act_quant", "gemm_down", "copy"],
-                    help="run one kernel of the dense step --reps times and exit (for rocprofv3 counters)")
+    ap.add_argument("--only", choices=["act_quant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
+                                       "copy", "routed_experts"],
+                    help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
+                         "(for rocprofv3)")
     ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -502,7 +531,7 @@ def main():
     total_flop = fl_up + fl_dn
     value = total_flop / (step_ms * 1e-3) / 1e12
     k = dense_kernels(st, T)
-    up_us = T.avg_us("gemm_up")
+    up_us = T.avg_us("gemm_up_gate")
     achieved = fl_up / up_us / 1e6
     traffic = recorded_traffic()
     line = {
@@ -518,10 +547,11 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantised to e4m3 with 128x128 scales)",
-        "config": {"workload": "dense FFN prefill: act_quant [4096,7168] -> gemm [w1;w3] 4096x36864x7168 -> "
-                               "silu_mul_act_quant [4096,18432] -> gemm w2 4096x7168x18432",
+        "config": {"workload": "dense FFN prefill: act_quant [4096,7168] -> gemm [w1;w3] 4096x36864x7168 with "
+                               "SiLU gate + act_quant epilogue -> gemm w2 4096x7168x18432",
                    "tokens": M, "dim": D, "inter": F, "block": 128},
-        "roofline": {"bound": "mfma", "kernel": "gemm_up 4096x36864x7168", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": "gemm_up_gate 4096x36864x7168 (gated epilogue)",
+                     "achieved": round(achieved, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic, "avg_launch_us": round(up_us, 1)},
         "kernels": k,
@@ -533,6 +563,8 @@ def main():
         del st
         torch.cuda.empty_cache()
         others["dense_ffn_ue8m0"] = bench_dense_ue8m0(dev, 20)
+        torch.cuda.empty_cache()
+        others["dense_ffn_unfused"] = bench_dense_unfused(dev, 20)
         torch.cuda.empty_cache()
         others["dense_ffn_bf16_path"] = bench_bf16_path(dev, 10)
         torch.cuda.empty_cache()

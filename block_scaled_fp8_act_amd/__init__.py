@@ -240,6 +240,78 @@ def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None, scale_fmt="f
     return c
 
 
+def _glu_outputs(M, F, device, out, return_h):
+    yo, so = out if out is not None else (None, None)
+    y = _out(yo, (M, F), torch.uint8, device, "y")
+    s = _scales_out(so, M, kblocks(F), device)
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=device) if return_h else None
+    return y, s, h
+
+
+def gemm_silu_mul_act_quant(a, a_s, w13, w13_s, scale_fmt="fp32", return_h=False, out=None):
+    """The gated up-projection in one kernel: ``act_quant(bf16(SiLU(h1) * h3))``
+    with ``h1 = gemm(a, a_s, w1, s1)`` and ``h3 = gemm(a, a_s, w3, s3)``, where
+    ``w13`` e4m3 ``[2F, K]`` stacks w1 over w3 and ``w13_s`` their scale grids
+    ``[2F/128, ceil(K/128)]``.  Equal to :func:`gemm` followed by
+    :func:`silu_mul_act_quant` on the two halves.  Returns ``(y, s)`` or
+    ``(y, s, h)``; ``out`` may supply ``(y, s)``.  ``scale_fmt`` applies to the
+    operand scales and to the scales produced."""
+    a = _mat(_bytes(a), "a", (torch.uint8,))
+    w = _mat(_bytes(w13), "w13", (torch.uint8,))
+    ars, aks = _scale_matrix(a_s, "a_s")
+    _mat(w13_s, "w13_s", (torch.float32,))
+    M, K = a.shape
+    N2, K2 = w.shape
+    if K2 != K or N2 % 2:
+        raise Dsfp8Error(f"w13 must be [2F, {K}], got {tuple(w.shape)}")
+    F = N2 // 2
+    if tuple(a_s.shape) != (M, kblocks(K)) or tuple(w13_s.shape) != (kblocks(N2), kblocks(K)):
+        raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and w13_s [2F/128, ceil(K/128)]")
+    y, s, h = _glu_outputs(M, F, a.device, out, return_h)
+    srs, sks = _scale_strides(s)
+    st = _lib.load().dsfp8_gemm_silu_mul_act_quant(
+        a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, w.data_ptr(), _ld(w), w13_s.data_ptr(), _ld(w13_s),
+        M, F, K, y.data_ptr(), _ld(y), s.data_ptr(), srs, sks, h.data_ptr() if h is not None else None, F,
+        _fmt(scale_fmt), _stream(a))
+    _check("gemm_silu_mul_act_quant", st)
+    return (y, s, h) if return_h else (y, s)
+
+
+def grouped_gemm_silu_mul_act_quant(a, a_s, w13, w13_s, offsets, scale_fmt="fp32", return_h=False, out=None,
+                                    workspace=None):
+    """Grouped form of :func:`gemm_silu_mul_act_quant`: rows
+    ``offsets[e]:offsets[e+1]`` of A use expert e's stacked ``w13[e]`` e4m3
+    ``[2F, K]`` and ``w13_s[e]`` ``[2F/128, ceil(K/128)]``."""
+    a = _mat(_bytes(a), "a", (torch.uint8,))
+    w = _mat(_bytes(w13), "w13", (torch.uint8,), dim=3)
+    ars, aks = _scale_matrix(a_s, "a_s")
+    _mat(w13_s, "w13_s", (torch.float32,), dim=3)
+    if not offsets.is_cuda or offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise Dsfp8Error("offsets must be a contiguous int32 CUDA tensor of length E+1")
+    M, K = a.shape
+    E, N2, K2 = w.shape
+    if K2 != K or N2 % 2 or offsets.numel() != E + 1:
+        raise Dsfp8Error("shape mismatch between a, w13 and offsets")
+    if not w.is_contiguous() or not w13_s.is_contiguous():
+        raise Dsfp8Error("Input tensor must be contiguous (w13, w13_s)")
+    F = N2 // 2
+    if tuple(w13_s.shape) != (E, kblocks(N2), kblocks(K)) or tuple(a_s.shape) != (M, kblocks(K)):
+        raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and w13_s [E, 2F/128, ceil(K/128)]")
+    lib = _lib.load()
+    y, s, h = _glu_outputs(M, F, a.device, out, return_h)
+    srs, sks = _scale_strides(s)
+    wsb = lib.dsfp8_grouped_gemm_workspace_bytes(E, M, N2, K)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+    st = lib.dsfp8_grouped_gemm_silu_mul_act_quant(
+        a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, w.data_ptr(), K, w13_s.data_ptr(), kblocks(K),
+        offsets.data_ptr(), E, M, F, K, y.data_ptr(), _ld(y), s.data_ptr(), srs, sks,
+        h.data_ptr() if h is not None else None, F, _fmt(scale_fmt), workspace.data_ptr(), workspace.numel(),
+        _stream(a))
+    _check("grouped_gemm_silu_mul_act_quant", st)
+    return (y, s, h) if return_h else (y, s)
+
+
 # ---- routed experts ------------------------------------------------------------------
 
 def act_quant_rows(x, rows, scale_fmt="fp32", out=None):

@@ -93,6 +93,7 @@ const char* dsfp8_status_string(dsfp8_status st) {
     case DSFP8_ERR_WORKSPACE: return "workspace is smaller than required";
     case DSFP8_ERR_LAUNCH: return "the HIP runtime reported a launch failure";
     case DSFP8_ERR_DTYPE: return "unknown element type";
+    case DSFP8_ERR_UNSUPPORTED: return "the fused form does not support this operand layout";
     default: return "unknown status";
   }
 }
@@ -279,6 +280,87 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   a.tile_start = static_cast<int32_t*>(workspace);
   a.pow2 = scale_fmt == DSFP8_SCALE_UE8M0;
   return launched(dsfp8::launch_grouped_gemm(a, stream));
+}
+
+namespace {
+
+// Arguments of the gated product, checked as the product and the quantiser
+// check theirs; E experts of 2F weight rows each (E = 1: the dense form).
+dsfp8_status glu_args(const void* A, int64_t lda, const float* a_s, int64_t as_rs, int64_t as_ks, const void* W13,
+                      int64_t ldw, const float* w_s, int64_t ldws, int64_t E, int64_t M, int64_t F, int64_t K,
+                      void* y, int64_t ldy, float* s, int64_t s_rs, int64_t s_ks, void* h, int64_t ldh,
+                      int scale_fmt, dsfp8::GemmArgs& a) {
+  if (!dim_ok(M) || !dim_ok(F) || !dim_ok(K) || !dim_ok(2 * F)) return DSFP8_ERR_SHAPE;
+  if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
+  DSFP8_TRY(check_mat(A, M, K, lda, 1));
+  DSFP8_TRY(check_scales(a_s, M, nblk(K), as_rs, as_ks));
+  DSFP8_TRY(check_mat(W13, E * 2 * F, K, ldw, 1));
+  DSFP8_TRY(check_mat(w_s, E * nblk(2 * F), nblk(K), ldws, 4));
+  DSFP8_TRY(check_quant_out(M, F, y, ldy, s, s_rs, s_ks));
+  if (h != nullptr) DSFP8_TRY(check_mat(h, M, F, ldh, 2));
+  a = dsfp8::GemmArgs{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.lda = lda;
+  a.a_s = a_s;
+  a.as_rs = as_rs;
+  a.as_ks = as_ks;
+  a.B = static_cast<const uint8_t*>(W13);
+  a.ldb = ldw;
+  a.b_s = w_s;
+  a.ldbs = ldws;
+  a.M = M;
+  a.N = 2 * F;
+  a.K = K;
+  a.pow2 = scale_fmt == DSFP8_SCALE_UE8M0;
+  a.glu_f = F;
+  a.qy = static_cast<uint8_t*>(y);
+  a.ldqy = ldy;
+  a.qs = s;
+  a.qs_rs = s_rs;
+  a.qs_ks = s_ks;
+  a.qh = static_cast<uint16_t*>(h);
+  a.ldqh = h ? ldh : 0;
+  a.q_ue8m0 = scale_fmt == DSFP8_SCALE_UE8M0;
+  if (M > 0 && F > 0 && !dsfp8::gemm_glu_supported(a)) return DSFP8_ERR_UNSUPPORTED;
+  return DSFP8_OK;
+}
+
+}  // namespace
+
+dsfp8_status dsfp8_gemm_silu_mul_act_quant(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
+                                           int64_t as_kb_stride, const void* W13, int64_t ldw, const float* w_s,
+                                           int64_t ldws, int64_t M, int64_t F, int64_t K, void* y, int64_t ldy,
+                                           float* s, int64_t s_row_stride, int64_t s_kb_stride, void* h,
+                                           int64_t ldh, int scale_fmt, hipStream_t stream) {
+  dsfp8::GemmArgs a;
+  DSFP8_TRY(glu_args(A, lda, a_s, as_row_stride, as_kb_stride, W13, ldw, w_s, ldws, 1, M, F, K, y, ldy, s,
+                     s_row_stride, s_kb_stride, h, ldh, scale_fmt, a));
+  if (M == 0 || F == 0) return DSFP8_OK;
+  return launched(dsfp8::launch_gemm_glu(a, stream));
+}
+
+dsfp8_status dsfp8_grouped_gemm_silu_mul_act_quant(const void* A, int64_t lda, const float* a_s,
+                                                   int64_t as_row_stride, int64_t as_kb_stride, const void* W13,
+                                                   int64_t ldw, const float* w_s, int64_t ldws,
+                                                   const int32_t* offsets, int64_t E, int64_t M_total, int64_t F,
+                                                   int64_t K, void* y, int64_t ldy, float* s, int64_t s_row_stride,
+                                                   int64_t s_kb_stride, void* h, int64_t ldh, int scale_fmt,
+                                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
+  if (offsets == nullptr) return DSFP8_ERR_NULL;
+  if (!al(offsets, 4)) return DSFP8_ERR_ALIGN;
+  dsfp8::GemmArgs a;
+  DSFP8_TRY(glu_args(A, lda, a_s, as_row_stride, as_kb_stride, W13, ldw, w_s, ldws, E, M_total, F, K, y, ldy, s,
+                     s_row_stride, s_kb_stride, h, ldh, scale_fmt, a));
+  const size_t need = dsfp8_grouped_gemm_workspace_bytes(E, M_total, 2 * F, K);
+  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
+  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
+  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
+  if (M_total == 0 || F == 0) return DSFP8_OK;
+  a.offsets = offsets;
+  a.E = E;
+  a.tile_start = static_cast<int32_t*>(workspace);
+  return launched(dsfp8::launch_grouped_gemm_glu(a, stream));
 }
 
 dsfp8_status dsfp8_act_quant_rows(const void* x, int64_t x_rows, int64_t ldx, const int32_t* rows, int64_t M,

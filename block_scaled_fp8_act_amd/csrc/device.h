@@ -26,6 +26,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// SiLU(g) * u in fp32 with the hardware exponential and reciprocal (each
+// within a few fp32 ulp, far below the bf16 rounding that follows), rounded
+// to bf16 and widened back, so that a quantiser applied next sees exactly the
+// bf16 value h (also returned in *hb).  For very negative g, e = inf and the
+// reciprocal gives -0 as g / inf would.  The standalone gate kernel and the
+// gated product's epilogue both use this one definition, so they agree bit
+// for bit on the same bf16 inputs.
+__device__ __forceinline__ float silu_mul_bf16(float g, float u, __bf16* hb) {
+  const float e = __expf(-g);
+  const float h = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
+  *hb = (__bf16)h;
+  return (float)(*hb);
+}
+
 // ---- e4m3 --------------------------------------------------------------------
 
 // Encode four fp32 values to e4m3fn bytes (nearest-even, v_cvt_pk_fp8_f32),

@@ -97,9 +97,26 @@ struct GemmArgs {
   float* partial;
   // every scale is a power of two: the MFMA applies them (exponents only)
   bool pow2;
+  // gated form: B stacks w1 (rows 0..F-1) over w3 (rows F..2F-1), N = 2F; the
+  // epilogue computes h = bf16(SiLU(bf16(x w1^T)) * bf16(x w3^T)) and writes
+  // act_quant(h) as e4m3 qy [M, F] and fp32 scales qs (element (m, b) at
+  // qs[m * qs_rs + b * qs_ks]), and h itself to qh when that is not null.
+  int64_t glu_f;  // F (0: plain product into C)
+  uint8_t* qy;
+  int64_t ldqy;
+  float* qs;
+  int64_t qs_rs, qs_ks;
+  uint16_t* qh;
+  int64_t ldqh;
+  bool q_ue8m0;
 };
 
 hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream);
+// Gated products: false if the operands do not fit the direct-to-LDS pipeline
+// the gated epilogue is built on (nothing launched).
+bool gemm_glu_supported(const GemmArgs& a);
+hipError_t launch_gemm_glu(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_grouped_gemm_glu(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_route(RouteArgs a, hipStream_t stream);
 size_t route_workspace_bytes(int64_t n, int64_t E);
 hipError_t launch_combine(CombineArgs a, hipStream_t stream);

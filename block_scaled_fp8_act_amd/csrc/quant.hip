@@ -100,18 +100,6 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&v)[8]) {
   v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
 }
 
-// SiLU(g) * u in fp32 with the hardware exponential and reciprocal (each
-// within a few fp32 ulp, far below the bf16 rounding that follows), rounded
-// to bf16 and widened back, so that the quantiser sees exactly the bf16 value
-// h.  For very negative g, e = inf and the reciprocal gives -0 as g / inf
-// would.
-__device__ __forceinline__ float silu_mul_bf16(float g, float u, __bf16* hb) {
-  const float e = __expf(-g);
-  const float h = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
-  *hb = (__bf16)h;
-  return (float)(*hb);
-}
-
 // A wave-unit is (row group g, K-block b): DPP row r of the wave (lanes
 // 16r..16r+15) quantises row 4g + r of block b.  Wave-units are numbered
 // block-major (w = b * G + g), so consecutive waves read consecutive row

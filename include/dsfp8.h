@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSFP8_ABI_VERSION 3
+#define DSFP8_ABI_VERSION 4
 #define DSFP8_BLOCK 128
 
 typedef int dsfp8_status;
@@ -72,7 +72,8 @@ enum {
   DSFP8_ERR_SCALE_FMT = -5,  /* unknown scale format                              */
   DSFP8_ERR_WORKSPACE = -6,  /* workspace smaller than the size query returned    */
   DSFP8_ERR_LAUNCH = -7,     /* the HIP runtime reported a launch failure         */
-  DSFP8_ERR_DTYPE = -8       /* unknown input element type                        */
+  DSFP8_ERR_DTYPE = -8,      /* unknown input element type                        */
+  DSFP8_ERR_UNSUPPORTED = -9 /* a fused form does not support this operand layout */
 };
 
 /* Scale formats.  UE8M0 rounds each scale value up to a power of two
@@ -238,6 +239,65 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K);
+
+/*
+ * Gated up-projection: the block-scaled FP8 product with the SiLU gate and
+ * the next activation quantisation in its epilogue, i.e. the feed-forward
+ * step w2(SiLU(w1 x) * w3 x) of [AG] 1.2 (MLP and Expert rows) up to the input
+ * of w2, with linear() of [AG] 6.3 / 8.5.3 for w1 and w3 and act_quant of
+ * [AG] 8.5.1 for the w2 input:
+ *   h1 = dsfp8_gemm(A, a_s, W13[0:F], w_s[0:F/128])         bf16 [M, F]
+ *   h3 = dsfp8_gemm(A, a_s, W13[F:2F], w_s[F/128:2F/128])   bf16 [M, F]
+ *   h  = bf16(SiLU(h1) * h3)          as dsfp8_silu_mul_act_quant
+ *   (y, s) = act_quant(h)             as dsfp8_act_quant
+ * without writing h1 or h3 to memory.  The result equals
+ * dsfp8_gemm(A, a_s, W13, w_s) followed by dsfp8_silu_mul_act_quant on its two
+ * halves (same arithmetic, same order).
+ *
+ *   A      e4m3 [M, K], row stride lda                    (device, read)
+ *   a_s    fp32 [M, KB(K)], strides as for dsfp8_gemm     (device, read)
+ *   W13    e4m3 [2F, K], row stride ldw: w1 in rows 0..F-1, w3 in rows
+ *          F..2F-1 (the two weights stacked)               (device, read)
+ *   w_s    fp32 [2F/128, KB(K)], row stride ldws (the two scale grids
+ *          stacked likewise)                               (device, read)
+ *   y      e4m3 [M, F], row stride ldy                    (device, written)
+ *   s      fp32 [M, F/128], strides s_row_stride, s_kb_stride (device, written)
+ *   h      bf16 [M, F], row stride ldh, or NULL           (device, written if not NULL)
+ *   scale_fmt  applies to both the product's operand scales (as for
+ *          dsfp8_gemm) and the scales written to s (as for dsfp8_act_quant).
+ * Supported layouts (else DSFP8_ERR_UNSUPPORTED; use the unfused calls):
+ * F a positive multiple of 128; K, lda, ldw multiples of 16; A and W13
+ * 16-byte aligned; (F + 128) * ldw + K < 2^31; y 8-byte aligned with ldy a
+ * multiple of 8; h (if given) 16-byte aligned with ldh a multiple of 8.
+ * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, UNSUPPORTED, LAUNCH.
+ */
+dsfp8_status dsfp8_gemm_silu_mul_act_quant(const void* A, int64_t lda,
+                                           const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
+                                           const void* W13, int64_t ldw, const float* w_s, int64_t ldws,
+                                           int64_t M, int64_t F, int64_t K,
+                                           void* y, int64_t ldy,
+                                           float* s, int64_t s_row_stride, int64_t s_kb_stride,
+                                           void* h, int64_t ldh, int scale_fmt, hipStream_t stream);
+
+/*
+ * Grouped form of dsfp8_gemm_silu_mul_act_quant over per-expert row ranges
+ * ([AG] 6.4 / 8.4): rows offsets[e]..offsets[e+1]-1 of A use expert e's
+ * stacked weight W13[e] [2F, K] (expert stride 2F*ldw) and scales w_s[e]
+ * [2F/128, KB(K)] (expert stride (2F/128)*ldws).  offsets as for
+ * dsfp8_grouped_gemm (device memory, not validated, clamped).  workspace:
+ * at least dsfp8_grouped_gemm_workspace_bytes(E, M_total, 2F, K) bytes.
+ * Supported layouts as above.
+ * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, WORKSPACE, UNSUPPORTED, LAUNCH.
+ */
+dsfp8_status dsfp8_grouped_gemm_silu_mul_act_quant(const void* A, int64_t lda,
+                                                   const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
+                                                   const void* W13, int64_t ldw, const float* w_s, int64_t ldws,
+                                                   const int32_t* offsets, int64_t E, int64_t M_total,
+                                                   int64_t F, int64_t K,
+                                                   void* y, int64_t ldy,
+                                                   float* s, int64_t s_row_stride, int64_t s_kb_stride,
+                                                   void* h, int64_t ldh, int scale_fmt,
+                                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * act_quant of gathered rows: the expert inputs x[idx] of [AG] 6.4 / 8.4

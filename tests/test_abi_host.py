@@ -17,7 +17,7 @@ from block_scaled_fp8_act_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsfp8.h")
 
-OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 P = 0x10000          # a fake, 256-byte aligned device address (never dereferenced)
 
 
@@ -49,7 +49,7 @@ def test_exports_every_declared_function(lib):
 
 def test_abi_version_and_strings(lib):
     assert lib.dsfp8_abi_version() == header_constant("#define DSFP8_ABI_VERSION")
-    for st in (OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE):
+    for st in (OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE, UNSUP):
         s = lib.dsfp8_status_string(st)
         assert s and s != b"unknown status"
     assert lib.dsfp8_status_string(12345) == b"unknown status"
@@ -58,7 +58,8 @@ def test_abi_version_and_strings(lib):
 def test_status_codes_match_header():
     for name, v in [("DSFP8_ERR_NULL", NULL), ("DSFP8_ERR_SHAPE", SHAPE), ("DSFP8_ERR_LD", LD),
                     ("DSFP8_ERR_ALIGN", ALIGN), ("DSFP8_ERR_SCALE_FMT", FMT), ("DSFP8_ERR_WORKSPACE", WS),
-                    ("DSFP8_ERR_LAUNCH", LAUNCH), ("DSFP8_ERR_DTYPE", DTYPE)]:
+                    ("DSFP8_ERR_LAUNCH", LAUNCH), ("DSFP8_ERR_DTYPE", DTYPE),
+                    ("DSFP8_ERR_UNSUPPORTED", UNSUP)]:
         assert header_constant(name) == v
 
 
@@ -194,3 +195,65 @@ def test_routed_expert_validation(lib):
     assert q(P, 8, 256, P + 2, 4, 256, P, 256, P, 1, 4, 0, None) == ALIGN
     assert q(P, 8, 256, P, 4, 256, P, 256, P, 1, 4, 7, None) == FMT
     assert q(P, 8, 255, P, 4, 256, P, 256, P, 1, 4, 0, None) == LD
+
+
+GLU_NAMES = ["A", "lda", "a_s", "as_rs", "as_ks", "W", "ldw", "w_s", "ldws", "M", "F", "K", "y", "ldy", "s", "srs",
+             "sks", "h", "ldh", "fmt", "stream"]
+GLU_ARGS = [P, 256, P, 1, 8, P, 256, P, 2, 8, 256, 256, P, 256, P, 1, 8, None, 0, 0, None]
+
+
+def glu_call(lib, **kw):
+    a = list(GLU_ARGS)
+    for k, v in kw.items():
+        a[GLU_NAMES.index(k)] = v
+    return lib.dsfp8_gemm_silu_mul_act_quant(*a)
+
+
+def test_gated_product_validation(lib):
+    assert glu_call(lib, fmt=3) == FMT
+    assert glu_call(lib, M=-1) == SHAPE
+    assert glu_call(lib, F=1 << 31) == SHAPE
+    assert glu_call(lib, A=None) == NULL
+    assert glu_call(lib, W=None) == NULL
+    assert glu_call(lib, y=None) == NULL
+    assert glu_call(lib, ldw=255) == LD
+    assert glu_call(lib, ldws=1) == LD            # the stacked scale grid has 2 columns
+    assert glu_call(lib, ldy=200) == LD
+    assert glu_call(lib, h=P, ldh=100) == LD
+    assert glu_call(lib, s=P + 2) == ALIGN
+    # layouts outside the fused kernel's pipeline: reported, nothing launched
+    assert glu_call(lib, F=200, ldy=200) == UNSUP                  # F not a multiple of 128
+    assert glu_call(lib, K=250, lda=256, ldw=256) == UNSUP         # K % 16 != 0
+    assert glu_call(lib, lda=264) == UNSUP                         # lda % 16 != 0
+    assert glu_call(lib, A=P + 8) == UNSUP                         # A not 16-byte aligned
+    assert glu_call(lib, y=P + 4) == UNSUP                         # y rows written 8 bytes at a time
+    assert glu_call(lib, ldy=260) == UNSUP
+    assert glu_call(lib, h=P + 8, ldh=256) == UNSUP
+    # one buffer descriptor spans w1 row n0 to w3 row F + n0 + 127: more than 2^31 bytes is not supported
+    assert glu_call(lib, F=1 << 20, ldw=4096, K=4096, lda=4096, ldws=32, ldy=1 << 20, sks=8) == UNSUP
+    # empty problems launch nothing
+    assert glu_call(lib, M=0) == OK
+    assert glu_call(lib, F=0, ldy=0) == OK
+
+
+def test_grouped_gated_product_validation(lib):
+    g = lib.dsfp8_grouped_gemm_silu_mul_act_quant
+    names = ["A", "lda", "a_s", "as_rs", "as_ks", "W", "ldw", "w_s", "ldws", "offsets", "E", "M", "F", "K", "y",
+             "ldy", "s", "srs", "sks", "h", "ldh", "fmt", "ws", "wsb", "stream"]
+    args = [P, 256, P, 1, 100, P, 256, P, 2, P, 4, 100, 256, 256, P, 256, P, 1, 100, None, 0, 0, P, 1 << 20, None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return g(*a)
+
+    assert call(E=0) == SHAPE
+    assert call(E=65537) == SHAPE
+    assert call(offsets=None) == NULL
+    assert call(offsets=P + 2) == ALIGN
+    assert call(fmt=7) == FMT
+    assert call(wsb=0) == WS
+    assert call(ws=None) == NULL
+    assert call(F=200, ldy=200) == UNSUP
+    assert call(M=0) == OK
