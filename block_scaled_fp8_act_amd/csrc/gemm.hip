@@ -867,22 +867,55 @@ __device__ __forceinline__ void expert_rows(const int32_t* offsets, int64_t e, i
   hi = b;
 }
 
-// Tile schedules for up to kMaxClasses row-tile heights: for class c,
-// tile_start[c * (E + 1) + e] = number of bm[c]-row tiles of the experts before
-// e whose row count lies in (lo[c], hi[c]].  One workgroup.
+// Tile classes of the grouped product.  With one class, every expert's rows
+// run in tiles of height h[0].  With three (heights h0 < h1 < h2), an expert
+// with at most h0 rows is class 0's and one with at most h1 rows class 1's;
+// a larger expert runs whole h2-row tiles in class 2, and a remainder of at
+// most h1 rows after its last whole tile goes to the class of that height
+// instead of padding one more h2-row tile (a larger remainder takes the
+// padded h2 tile).  class_rows gives the rows [lo, hi), relative to the
+// expert's first row, that class c computes for an expert of n rows.
 constexpr int kMaxClasses = 3;
-struct ScheduleClasses {
-  int n;
-  int bm[kMaxClasses];
-  int64_t lo[kMaxClasses], hi[kMaxClasses];
-};
+__device__ __forceinline__ void class_rows(int64_t n, int c, int classes, const int (&h)[3], int64_t& lo,
+                                           int64_t& hi) {
+  lo = hi = 0;
+  if (classes == 1) {
+    if (c == 0) hi = n;
+    return;
+  }
+  int64_t split = 0;  // class 2 computes [0, split), class rc computes [split, n)
+  int rc = -1;
+  if (n <= h[0]) {
+    rc = 0;
+  } else if (n <= h[1]) {
+    rc = 1;
+  } else {
+    const int64_t full = n / h[2], rem = n - full * h[2];
+    if (full > 0 && rem > 0 && rem <= h[1]) {
+      split = full * h[2];
+      rc = rem <= h[0] ? 0 : 1;
+    } else {
+      split = n;
+    }
+  }
+  if (c == 2) {
+    hi = split;
+  } else if (c == rc) {
+    lo = split;
+    hi = n;
+  }
+}
 
-__global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* offsets, int64_t E, int64_t M,
-                                                             ScheduleClasses cls, int32_t* tile_start) {
+// tile_start[c * (E + 1) + e] = number of class-c row tiles of the experts
+// before e.  One workgroup.
+__global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmArgs p) {
+  const int32_t* offsets = p.offsets;
+  const int64_t E = p.E, M = p.M;
+  int32_t* tile_start = p.tile_start;
   __shared__ int32_t part[1024];
   __shared__ int32_t carry;
   const int t = threadIdx.x;
-  for (int c = 0; c < cls.n; ++c) {
+  for (int c = 0; c < p.grp_classes; ++c) {
     int32_t* ts = tile_start + (int64_t)c * (E + 1);
     if (t == 0) {
       carry = 0;
@@ -895,8 +928,9 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* offs
       if (e < E) {
         int64_t lo, hi;
         expert_rows(offsets, e, M, lo, hi);
-        const int64_t rows = hi - lo;
-        if (rows > cls.lo[c] && rows <= cls.hi[c]) cnt = (int32_t)((rows + cls.bm[c] - 1) / cls.bm[c]);
+        int64_t a, b;
+        class_rows(hi - lo, c, p.grp_classes, p.grp_h, a, b);
+        cnt = (int32_t)((b - a + p.grp_h[c] - 1) / p.grp_h[c]);
       }
       part[t] = cnt;
       __syncthreads();
@@ -914,19 +948,19 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* offs
   }
 }
 
-// One workgroup per (row tile of an expert, 128-column tile).  The grid is
-// sized for the worst case; the real number of row tiles is ts[E].  Ids past
-// the real work exit at once; the rest are renumbered XCD-contiguously over
-// the real work, column tile fastest, so an expert's rows are fetched once per
-// XCD and reused across its column tiles, and consecutive row tiles of a large
-// expert share each weight tile in L2.
-template <class CF, int VEC, bool GLU = false>
-__global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
+// One workgroup per (row tile of an expert, column tile).  The grid is sized
+// for the worst case; the real number of row tiles is ts[E].  Ids past the
+// real work exit at once; the rest are renumbered XCD-contiguously over the
+// real work, column tile fastest, so an expert's rows are fetched once per
+// XCD and reused across its column tiles, and consecutive row tiles of a
+// large expert share each weight tile in L2.  pid is the workgroup's index
+// within its launch range, which starts at a multiple of 8 (so pid % 8 is
+// still its XCD).
+template <class CF, int VEC, bool GLU>
+__device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uint8_t* smem) {
   const int32_t* ts = p.tile_start;
   const int64_t tiles_n = col_tiles<CF, GLU>(p);
   const int64_t total = (int64_t)ts[p.E] * tiles_n;
-  const int64_t pid = blockIdx.x;
   if (pid >= total) return;
   const int64_t L = xcd_contiguous(pid, total);
   const int64_t slot = L / tiles_n;
@@ -947,13 +981,50 @@ __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) 
   t.a_s = p.a_s;
   t.B = p.B + e * p.N * p.ldb;
   t.b_s = p.b_s + e * kbn * p.ldbs;
-  t.row0 = r0 + (slot - ts[e]) * CF::BM;
-  t.row_end = r1;
+  int64_t clo, chi;
+  class_rows(r1 - r0, p.grp_class, p.grp_classes, p.grp_h, clo, chi);
+  t.row0 = r0 + clo + (slot - ts[e]) * CF::BM;
+  t.row_end = r0 + chi;
   t.n0 = tn * kColStep<CF, GLU>;
   t.kb0 = 0;
   t.kb1 = (int)((p.K + BK - 1) / BK);
   t.partial = nullptr;
   run_tile<CF, VEC, GLU>(p, t, smem);
+}
+
+template <class CF, int VEC, bool GLU = false>
+__global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
+  grouped_tile<CF, VEC, GLU>(p, blockIdx.x, smem);
+}
+
+// The three tile classes of the gated grouped product in one launch: ids
+// [0, n2) run class 2 (the tallest tiles, which take longest), then n1 ids of
+// class 1, then class 0, so the short tiles fill the CUs that the tall ones
+// leave idle at the end instead of waiting for a launch of their own.  All
+// three use 8 waves and one workgroup per CU (their LDS rings take 125 to
+// 149 KB), so sharing one kernel costs no occupancy.  n2 and n1 are
+// multiples of 8.  p holds the class-0 schedule; class c's is c*(E+1) later.
+template <class C0, class C1, class C2, int VEC>
+__global__ __launch_bounds__(C2::kThreads) void grouped_glu_kernel(GemmArgs p, int64_t n2, int64_t n1) {
+  static_assert(C0::kThreads == C2::kThreads && C1::kThreads == C2::kThreads, "one workgroup size");
+  constexpr int L01 = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
+  constexpr int LDS = L01 > C2::LDS_BYTES ? L01 : C2::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  const int64_t id = blockIdx.x;
+  GemmArgs q = p;
+  if (id < n2) {
+    q.grp_class = 2;
+    q.tile_start = p.tile_start + 2 * (p.E + 1);
+    grouped_tile<C2, VEC, true>(q, id, smem);
+  } else if (id < n2 + n1) {
+    q.grp_class = 1;
+    q.tile_start = p.tile_start + (p.E + 1);
+    grouped_tile<C1, VEC, true>(q, id - n2, smem);
+  } else {
+    q.grp_class = 0;
+    grouped_tile<C0, VEC, true>(q, id - n2 - n1, smem);
+  }
 }
 
 inline bool aligned(const void* q, size_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; }
@@ -1067,49 +1138,69 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);
 }
 
-// Grouped launches.  With the direct-to-LDS pipeline the experts are split
-// into three classes by their row count, each run with its own tile height
-// (C0::BM rows: up to C0::BM; C1::BM rows: up to C1::BM; C2 tiles: more), so
-// a row tile is never padded by more than its own height and a large expert
+// Grouped launches.  With the direct-to-LDS pipeline the rows are split into
+// three tile classes (class_rows), each run with its own tile height, so a
+// row tile is never padded by more than its own height and a large expert
 // streams its weight once per C2::BM rows instead of once per C0::BM.
 template <class C0, class C1, class C2, bool GLU>
 hipError_t grouped_classes(const GemmArgs& a, hipStream_t stream) {
   static_assert(C0::BM < C1::BM && C1::BM < C2::BM, "increasing tile heights");
-  ScheduleClasses cls{};
-  cls.n = 3;
-  cls.bm[0] = C0::BM; cls.lo[0] = 0;      cls.hi[0] = C0::BM;
-  cls.bm[1] = C1::BM; cls.lo[1] = C0::BM; cls.hi[1] = C1::BM;
-  cls.bm[2] = C2::BM; cls.lo[2] = C1::BM; cls.hi[2] = a.M;
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.E, a.M, cls, a.tile_start);
+  GemmArgs s = a;
+  s.grp_classes = 3;
+  s.grp_h[0] = C0::BM;
+  s.grp_h[1] = C1::BM;
+  s.grp_h[2] = C2::BM;
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t E = a.E, M = a.M;
   auto tiles_n = [&](int bn) { return GLU ? a.glu_f / BK : (a.N + bn - 1) / bn; };
   auto mn = [](int64_t x, int64_t y) { return x < y ? x : y; };
-  // Bounds on each class's row tiles: one per expert for the two small
-  // classes; for the large class at most M/C2::BM + (experts with > C1::BM rows).
-  GemmArgs c0 = a, c1 = a, c2 = a;
+  // Bounds on each class's row tiles: at most one per expert with at least 1
+  // (class 0) or C0::BM + 1 (class 1) rows; for the large class at most
+  // M/C2::BM whole tiles plus one padded tile per expert with > C1::BM rows.
+  GemmArgs c0 = s, c1 = s, c2 = s;
+  c0.grp_class = 0;
+  c1.grp_class = 1;
+  c2.grp_class = 2;
   c1.tile_start = a.tile_start + (E + 1);
   c2.tile_start = a.tile_start + 2 * (E + 1);
   const int64_t s0 = mn(E, M), s1 = mn(E, M / (C0::BM + 1));
   const int64_t s2 = (M + C2::BM - 1) / C2::BM + mn(E, M / (C1::BM + 1));
-  if (s0 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C0, GLU, dim3((unsigned)(s0 * tiles_n(C0::BN))), stream, c0);
-  if (s1 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C1, GLU, dim3((unsigned)(s1 * tiles_n(C1::BN))), stream, c1);
-  if (s2 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C2, GLU, dim3((unsigned)(s2 * tiles_n(C2::BN))), stream, c2);
-  return hipGetLastError();
+  if constexpr (GLU) {
+    auto up8 = [](int64_t v) { return (v + 7) / 8 * 8; };
+    const int64_t n2 = up8(s2 * tiles_n(C2::BN)), n1 = up8(s1 * tiles_n(C1::BN)), n0 = s0 * tiles_n(C0::BN);
+    const dim3 grid((unsigned)(n2 + n1 + n0)), blk(C2::kThreads);
+    const bool kfull = a.K % BK == 0;
+    if (a.pow2) {
+      if (kfull) hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, -2>), grid, blk, 0, stream, c0, n2, n1);
+      else hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, -3>), grid, blk, 0, stream, c0, n2, n1);
+    } else {
+      if (kfull) hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, 0>), grid, blk, 0, stream, c0, n2, n1);
+      else hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, -1>), grid, blk, 0, stream, c0, n2, n1);
+    }
+    return hipGetLastError();
+  } else {
+    if (s0 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C0, GLU, dim3((unsigned)(s0 * tiles_n(C0::BN))), stream, c0);
+    if (s1 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C1, GLU, dim3((unsigned)(s1 * tiles_n(C1::BN))), stream, c1);
+    if (s2 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C2, GLU, dim3((unsigned)(s2 * tiles_n(C2::BN))), stream, c2);
+    return hipGetLastError();
+  }
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.M == 0) return hipSuccess;
   if (pick_vec<CfgGrp>(a) <= 0 && pick_vec<CfgDma>(a) <= 0 && pick_vec<CfgDmaBig>(a) <= 0)
     return grouped_classes<CfgGrp, CfgDma, CfgDmaBig, false>(a, stream);
-  ScheduleClasses cls{};
-  cls.n = 1;
-  cls.bm[0] = Cfg128::BM; cls.lo[0] = 0; cls.hi[0] = a.M;
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.E, a.M, cls, a.tile_start);
+  static_assert(CfgDma::BM == Cfg128::BM, "one tile height for both pipelines");
+  GemmArgs s = a;
+  s.grp_class = 0;
+  s.grp_classes = 1;
+  s.grp_h[0] = Cfg128::BM;
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return dispatch<CfgDma, Cfg128, true>(a, grouped_grid<CfgDma>(a), grouped_grid<Cfg128>(a), stream);
+  return dispatch<CfgDma, Cfg128, true>(s, grouped_grid<CfgDma>(s), grouped_grid<Cfg128>(s), stream);
 }
 
 // ---- gated form ----------------------------------------------------------------

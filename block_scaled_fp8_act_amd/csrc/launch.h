@@ -92,7 +92,11 @@ struct GemmArgs {
   // grouped form only
   const int32_t* offsets;
   int64_t E;
-  int32_t* tile_start;  // workspace: E+1 ints
+  int32_t* tile_start;  // workspace: E+1 ints (this launch's tile class)
+  // tile classes of the grouped launches: this launch's class, the number of
+  // classes and their row-tile heights (increasing)
+  int grp_class, grp_classes;
+  int grp_h[3];
   // dense form with split K: fp32 partial products [splits, M, N] (workspace)
   float* partial;
   // every scale is a power of two: the MFMA applies them (exponents only)

@@ -274,8 +274,10 @@ def run_grouped(a, a_s, w, w_s, counts, fmt="fp32"):
 
 
 # Row counts that exercise the three tile heights (<= 64, 65..128, > 128 rows),
-# empty experts and single rows.
-GROUP_COUNTS = [0, 3, 64, 65, 128, 0, 129, 300, 1, 257]
+# remainders past whole 256-row tiles that run in the 64-row class (257, 300),
+# the 128-row class (400) or a padded 256-row tile (450), empty experts and
+# single rows.
+GROUP_COUNTS = [0, 3, 64, 65, 128, 0, 129, 300, 1, 257, 400, 450]
 
 
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])

@@ -60,6 +60,10 @@ def _check_all(C, a, a_s, b, b_s, off, what):
     ([0, 0, 129, 0], 64, 1000),
     ([130, 127, 128, 1, 255], 384, 256),
     ([70, 3, 300, 0, 129], 256, 272),  # partial last K-block on the direct-to-LDS path
+    # experts above 256 rows whose rows past the last whole 256-row tile run
+    # in the 64-row class (257, 320), the 128-row class (321, 356, 640), or
+    # a padded 256-row tile (700); 512 has no remainder
+    ([257, 320, 321, 356, 512, 640, 700, 5], 256, 256),
 ])
 @pytest.mark.parametrize("layout", ["kb", "row"])
 def test_grouped_small(counts, N, K, layout):
