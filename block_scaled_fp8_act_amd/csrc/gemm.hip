@@ -814,43 +814,49 @@ __global__ __launch_bounds__(CF::kThreads) void gemm_kernel(GemmArgs p) {
 }
 
 // Sum the split-K partials in split order (deterministic) and round to bf16.
-// Each thread owns four consecutive outputs and keeps eight splits' loads in
-// flight before adding them in order.
+// The kernel is bound by the latency of its loads, so each thread keeps
+// IN_FLIGHT splits' loads in flight before adding them in order: VEC = 4
+// (four consecutive outputs per thread, 16-byte loads, 8 splits at a time)
+// for few splits over many outputs, VEC = 1 (one output per thread, 32 splits
+// at a time) for many splits over few outputs.
+template <int VEC, int IN_FLIGHT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int splits) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VEC;
   const int64_t MN = p.M * p.N;
   if (i >= MN) return;
-  const bool full = i + 4 <= MN && (MN & 3) == 0;
-  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < splits; k0 += 8) {
-    float4 v[8];
+  const bool full = i + VEC <= MN && (MN % VEC) == 0;
+  float s[VEC];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int e = 0; e < VEC; ++e) s[e] = 0.0f;
+  for (int k0 = 0; k0 < splits; k0 += IN_FLIGHT) {
+    float v[IN_FLIGHT][VEC];
+#pragma unroll
+    for (int u = 0; u < IN_FLIGHT; ++u) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[u][e] = 0.0f;
       if (k0 + u < splits) {
         const float* src = p.partial + (int64_t)(k0 + u) * MN + i;
-        if (full) {
-          v[u] = *reinterpret_cast<const float4*>(src);
+        if (VEC == 4 && full) {
+          const float4 f = *reinterpret_cast<const float4*>(src);
+          v[u][0] = f.x;
+          v[u][VEC > 1 ? 1 : 0] = VEC > 1 ? f.y : v[u][0];
+          v[u][VEC > 2 ? 2 : 0] = VEC > 2 ? f.z : v[u][0];
+          v[u][VEC > 3 ? 3 : 0] = VEC > 3 ? f.w : v[u][0];
         } else {
-          v[u].x = src[0];
-          if (i + 1 < MN) v[u].y = src[1];
-          if (i + 2 < MN) v[u].z = src[2];
-          if (i + 3 < MN) v[u].w = src[3];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            if (i + e < MN) v[u][e] = src[e];
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (k0 + u < splits) {
-        s[0] += v[u].x;
-        s[1] += v[u].y;
-        s[2] += v[u].z;
-        s[3] += v[u].w;
-      }
-    }
+    for (int u = 0; u < IN_FLIGHT; ++u)
+      if (k0 + u < splits)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] += v[u][e];
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < VEC; ++e) {
     const int64_t idx = i + e;
     if (idx >= MN) break;
     const int64_t row = idx / p.N, col = idx - row * p.N;
@@ -1124,15 +1130,32 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     static_assert(CfgDma::BM == Cfg128::BM && CfgDma::BN == Cfg128::BN, "same split grid for both pipelines");
     dim3 g = dense_grid<CfgDma>(a);
     g.y = (unsigned)splits;
-    hipError_t err = dispatch<CfgDma, Cfg128, false>(a, g, g, stream);
+    hipError_t err;
+    if (a.M <= CfgGrp::BM && pick_vec<CfgGrp>(a) <= 0) {
+      // at most 64 rows: the 64-row tiles (same grid, one row tile)
+      static_assert(CfgGrp::BN == CfgDma::BN, "same column tiles");
+      DSFP8_LAUNCH_DMA(gemm_kernel, CfgGrp, false, g, stream, a);
+      err = hipGetLastError();
+    } else {
+      err = dispatch<CfgDma, Cfg128, false>(a, g, g, stream);
+    }
     if (err != hipSuccess) return err;
-    const int64_t groups = (a.M * a.N + 1023) / 1024;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
+    if (splits > 8) {
+      const int64_t groups = (a.M * a.N + 255) / 256;
+      hipLaunchKernelGGL((splitk_reduce_kernel<1, 32>), dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
+    } else {
+      const int64_t groups = (a.M * a.N + 1023) / 1024;
+      hipLaunchKernelGGL((splitk_reduce_kernel<4, 8>), dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
+    }
     return hipGetLastError();
   }
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) <= 0) {
     DSFP8_LAUNCH_DMA(gemm_kernel, CfgDmaBig, false, dense_grid<CfgDmaBig>(a), stream, a);
+    return hipGetLastError();
+  }
+  if (a.M <= CfgGrp::BM && pick_vec<CfgGrp>(a) <= 0) {
+    DSFP8_LAUNCH_DMA(gemm_kernel, CfgGrp, false, dense_grid<CfgGrp>(a), stream, a);
     return hipGetLastError();
   }
   return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);

@@ -159,7 +159,7 @@ def test_strided_operands():
     check_gemm_full(host_bits16(c), a, a_s, b, b_s, "strided")
 
 
-def _sampled_product(M, N, K, seed, row_pick, nblocks):
+def _sampled_product(M, N, K, seed, row_pick, nblocks, fmt="fp32"):
     """GEMM at full size with device-drawn inputs; compare sampled outputs.
 
     x and W are drawn on the device; the GPU quantises them; the oracle
@@ -167,24 +167,25 @@ def _sampled_product(M, N, K, seed, row_pick, nblocks):
     must agree bit-exactly with the GPU's bytes, and then supplies the
     reference product for those rows and columns.
     """
+    ue = fmt == "ue8m0"
     xf = I.device_normal((M, K), seed=seed, std=1.0, device="cuda", dtype=torch.bfloat16)
     wf = I.device_normal((N, K), seed=seed + 1, std=0.02, device="cuda")
-    a, a_s = ds.act_quant(xf)
-    b, b_s = ds.weight_quant(wf)
-    c = ds.gemm(a, a_s, b, b_s)
+    a, a_s = ds.act_quant(xf, fmt)
+    b, b_s = ds.weight_quant(wf, fmt)
+    c = ds.gemm(a, a_s, b, b_s, scale_fmt=fmt)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(seed).choice(M, row_pick, replace=False))
     rows[-1] = M - 1
     kb = (N + 127) // 128
     blks = sorted({0, kb - 1, *np.random.default_rng(seed + 2).choice(kb, nblocks, replace=False).tolist()})
     xr = xf[torch.from_numpy(rows).cuda()].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    ar, asr = Q.act_quant(xr)
+    ar, asr = Q.act_quant(xr, ue8m0=ue)
     assert np.array_equal(host_u8(a[torch.from_numpy(rows).cuda()]), ar)
     A_hat = G.dequant_act(ar, asr)
     for bi in blks:
         n0, n1 = bi * 128, min(N, bi * 128 + 128)
         wr = wf[n0:n1].cpu().numpy()
-        br, bsr = Q.weight_quant(wr)
+        br, bsr = Q.weight_quant(wr, ue8m0=ue)
         assert np.array_equal(host_u8(b[n0:n1]), br)
         W_hat = G.dequant_weight(br, bsr)
         Cg = host_bits16(c[torch.from_numpy(rows).cuda(), n0:n1])
@@ -193,6 +194,15 @@ def _sampled_product(M, N, K, seed, row_pick, nblocks):
 
 def test_dense_ffn_up_sampled():
     _sampled_product(4096, 18432, 7168, 50, 256, 4)
+
+
+def test_dense_ffn_up_sampled_ue8m0():
+    # power-of-two scales applied by the MFMA on the 256 x 256 tiles
+    _sampled_product(4096, 18432, 7168, 55, 256, 4, "ue8m0")
+
+
+def test_dense_ffn_down_sampled_ue8m0():
+    _sampled_product(4096, 7168, 18432, 75, 128, 3, "ue8m0")
 
 
 def test_dense_ffn_up_stacked_sampled():

@@ -228,34 +228,37 @@ def test_unsupported_layout_raises():
         ds.gemm_silu_mul_act_quant(a, a_s, w, w_s)
 
 
-def test_dense_ffn_full_size_sampled():
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_dense_ffn_full_size_sampled(fmt):
     """The dense feed-forward up-projection (4096 x 2*18432 x 7168) with
     device-drawn inputs: bit-identical to the unfused path everywhere, and
-    against the oracle on sampled rows and output blocks."""
+    against the oracle on sampled rows and output blocks, with fp32 and with
+    power-of-two (ue8m0) scales."""
     M, K, F_ = 4096, 7168, 18432
+    ue = fmt == "ue8m0"
     xf = I.device_normal((M, K), seed=80, std=1.0, device="cuda", dtype=torch.bfloat16)
     wf = I.device_normal((2 * F_, K), seed=81, std=0.02, device="cuda")
-    a, a_s = ds.act_quant(xf)
-    w, w_s = ds.weight_quant(wf)
-    fused = ds.gemm_silu_mul_act_quant(a, a_s, w, w_s, return_h=True)
-    assert_same(fused, unfused(a, a_s, w, w_s, "fp32"), "dense FFN size")
+    a, a_s = ds.act_quant(xf, fmt)
+    w, w_s = ds.weight_quant(wf, fmt)
+    fused = ds.gemm_silu_mul_act_quant(a, a_s, w, w_s, fmt, return_h=True)
+    assert_same(fused, unfused(a, a_s, w, w_s, fmt), "dense FFN size")
     y, s, h = fused
     rows = np.sort(np.random.default_rng(80).choice(M, 24, replace=False))
     rows[-1] = M - 1
     blocks = sorted({0, F_ // 128 - 1, *np.random.default_rng(81).choice(F_ // 128, 3, replace=False).tolist()})
     rt = torch.from_numpy(rows).cuda()
     xr = xf[rt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    ar, asr = Q.act_quant(xr)
+    ar, asr = Q.act_quant(xr, ue8m0=ue)
     assert np.array_equal(host_u8(a[rt]), ar)
     for j in blocks:
         sel = np.r_[j * 128:(j + 1) * 128, F_ + j * 128:F_ + (j + 1) * 128]
         wr = wf[torch.from_numpy(sel).cuda()].cpu().numpy()
-        wq, wsq = Q.weight_quant(wr)
+        wq, wsq = Q.weight_quant(wr, ue8m0=ue)
         # the GPU's weight quantiser agrees on these blocks (both halves)
         assert np.array_equal(host_u8(w[torch.from_numpy(sel).cuda()]), wq)
         cols = slice(j * 128, (j + 1) * 128)
         check_against_oracle(host_u8(y[rt, cols]), s[rt, j:j + 1].cpu().numpy(), host_bits16(h[rt, cols]),
-                             ar, asr, wq, wsq, False, f"dense FFN block {j}")
+                             ar, asr, wq, wsq, ue, f"dense FFN block {j} {fmt}")
 
 
 # ---- grouped ------------------------------------------------------------------------------
