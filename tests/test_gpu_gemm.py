@@ -192,6 +192,16 @@ def _sampled_product(M, N, K, seed, row_pick, nblocks, fmt="fp32"):
         check_product(Cg, A_hat @ W_hat.T, A_hat, W_hat, f"{M}x{N}x{K} block {bi}")
 
 
+@pytest.mark.parametrize("M,N,K,fmt", [(1, 4608, 7168, "fp32"), (16, 7168, 2048, "fp32"), (8, 1536, 7168, "ue8m0"),
+                                       (5, 300, 1040, "fp32"), (16, 129, 16, "ue8m0")])
+def test_decode_rows(M, N, K, fmt):
+    # at most 16 rows with K % 16 == 0: the kernel that splits K across the
+    # waves of one workgroup per 16 columns (ragged N and K included)
+    a, a_s, b, b_s = operands(M, N, K, I.DECODE_QA, ue8m0=(fmt == "ue8m0"), outliers=0.01)
+    for layout in ("kb", "row"):
+        check_gemm_full(run(a, a_s, b, b_s, layout, scale_fmt=fmt), a, a_s, b, b_s, f"{M}x{N}x{K} {fmt} {layout}")
+
+
 def test_dense_ffn_up_sampled():
     _sampled_product(4096, 18432, 7168, 50, 256, 4)
 
