@@ -1081,16 +1081,27 @@ __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uin
   const int64_t total = (int64_t)ts[p.E] * tiles_n;
   if (pid >= total) return;
   const int64_t L = xcd_contiguous(pid, total);
-  const int64_t slot = L / tiles_n;
-  const int64_t tn = L - slot * tiles_n;
-  // Last expert e with ts[e] <= slot; then ts[e+1] > slot.
-  int64_t lo = 0, hi = p.E;  // invariant: ts[lo] <= slot < ts[hi]
+  const int64_t slot0 = L / tiles_n;
+  // Last expert e with ts[e] <= slot0; then ts[e+1] > slot0.
+  int64_t lo = 0, hi = p.E;  // invariant: ts[lo] <= slot0 < ts[hi]
   while (hi - lo > 1) {
     const int64_t mid = (lo + hi) >> 1;
-    if (ts[mid] <= slot) lo = mid;
+    if (ts[mid] <= slot0) lo = mid;
     else hi = mid;
   }
   const int64_t e = lo;
+  // Expert e's row tiles x column tiles are one contiguous id range; inside
+  // it the ids run in groups of up to kGroupM row tiles, row tile fastest,
+  // so the concurrent tiles of a large expert share each weight panel as
+  // well as each activation panel in L2 (as the dense product's groups do).
+  const int64_t rt = ts[e + 1] - ts[e];
+  const int64_t l = L - (int64_t)ts[e] * tiles_n;
+  const int64_t per_group = (int64_t)kGroupM * tiles_n;
+  const int64_t g0 = l / per_group * kGroupM;
+  const int64_t gsize = rt - g0 < kGroupM ? rt - g0 : kGroupM;
+  const int64_t in = l - g0 * tiles_n;
+  const int64_t slot = ts[e] + g0 + in % gsize;
+  const int64_t tn = in / gsize;
   int64_t r0, r1;
   expert_rows(p.offsets, e, p.M, r0, r1);
   const int64_t kbn = (p.N + BK - 1) / BK;
