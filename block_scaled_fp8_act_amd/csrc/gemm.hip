@@ -473,15 +473,16 @@ struct DmaCfg {
 };
 
 // Large products: 256x256 tiles, 8 waves of 128x64 (one workgroup per CU);
-// small or skinny products and the grouped form: 128x128 tiles, 4 waves of
-// 64x64 (two workgroups per CU).
+// products with too few of those tiles, split-K products and the grouped
+// form's 65-128-row class: 128x128 tiles, 4 waves of 64x64 (two workgroups
+// per CU).
 #ifndef DSFP8_DMA_TILE
 #define DSFP8_DMA_TILE 256, 256, 2, 4, 2
 #endif
 using CfgDmaBig = DmaCfg<DSFP8_DMA_TILE>;
 using CfgDma = DmaCfg<128, 128, 2, 2, 2>;
-// Grouped form: 64-row tiles (the routed rows of most experts fill less than
-// one), 4 waves of 64x32.
+// Grouped form's class of at most 64 rows, and dense products of 17 to 64
+// rows: 64-row tiles, 4 waves of 64x32.
 #ifndef DSFP8_GROUPED_TILE
 #define DSFP8_GROUPED_TILE 64, 128, 1, 4, 2
 #endif
@@ -866,34 +867,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 
 // Products with at most 16 rows (decode at small batch): the weight is
 // streamed once and every output needs all of K, so one workgroup of
-// kSkinnyWaves waves owns 16 output columns over the whole of K.  Its waves take the K-blocks in turn
-// (wave w: w, w + W, ...), load their MFMA operands straight from memory into
-// registers (the weight with nontemporal loads, kSkinnyDepth K-blocks in
-// flight), and multiply one 16-column weight fragment by the two 16-row
-// activation fragments per K-block; the per-wave sums are then added in wave
-// order through LDS and rounded to bf16.  No split of K across workgroups,
-// so no fp32 partials and no second kernel.
+// kSkinnyWaves waves owns 16 output columns over the whole of K.  Its waves
+// take the K-blocks in turn (wave w: w, w + W, ...), load their MFMA operands
+// straight from memory into registers (kSkinnyDepth K-blocks in flight;
+// nontemporal loads of the weight measured 8% slower), and multiply the
+// 16-column weight fragment by the 16-row activation fragment per K-block;
+// the per-wave sums are then added in wave order through LDS and rounded to
+// bf16.  No split of K across workgroups, so no fp32 partials and no second
+// kernel.
 #ifndef DSFP8_SKINNY
 #define DSFP8_SKINNY 16, 3
 #endif
 constexpr int kSkinnyCfg[2] = {DSFP8_SKINNY};
 constexpr int kSkinnyWaves = kSkinnyCfg[0];
 constexpr int kSkinnyDepth = kSkinnyCfg[1];
+constexpr int kSkinnyRows = 16;
 
 // 32 bytes of one operand row for a lane: two 16-byte chunks; a chunk at or
 // past K (K is a multiple of 16 here) or of a row outside the matrix reads as
 // zero.
-template <bool NT>
 __device__ __forceinline__ v8i skinny_frag(const uint8_t* row, bool valid, int64_t k, int64_t K) {
   u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-  if (valid && k < K) {
-    lo = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + k))
-            : *reinterpret_cast<const u32x4*>(row + k);
-  }
-  if (valid && k + 16 < K) {
-    hi = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + k + 16))
-            : *reinterpret_cast<const u32x4*>(row + k + 16);
-  }
+  if (valid && k < K) lo = *reinterpret_cast<const u32x4*>(row + k);
+  if (valid && k + 16 < K) hi = *reinterpret_cast<const u32x4*>(row + k + 16);
   v8i f;
   f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
   f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
@@ -902,7 +898,7 @@ __device__ __forceinline__ v8i skinny_frag(const uint8_t* row, bool valid, int64
 
 template <bool POW2>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs p) {
-  __shared__ float red[kSkinnyWaves][2][64][4];
+  __shared__ float red[kSkinnyWaves][64][4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, fg = lane >> 4;
@@ -910,69 +906,56 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
   const int64_t K = p.K;
   const int64_t nk = (K + BK - 1) / BK;
   // Column layout (weight fragment first): lane (fr, fg) ends with outputs
-  // C[16i + fr][n0 + 4fg + v]; it loads weight row n0 + fr and activation
-  // rows fr and 16 + fr, bytes 32fg .. 32fg + 31 of each K-block.
-  const bool bv = n0 + fr < p.N, av0 = fr < p.M, av1 = 16 + fr < p.M;
+  // C[fr][n0 + 4fg + v]; it loads weight row n0 + fr and activation row fr,
+  // bytes 32fg .. 32fg + 31 of each K-block.
+  const bool bv = n0 + fr < p.N, av = fr < p.M;
   const uint8_t* brow = p.B + (bv ? n0 + fr : 0) * p.ldb;
-  const uint8_t* arow0 = p.A + (av0 ? fr : 0) * p.lda;
-  const uint8_t* arow1 = p.A + (av1 ? 16 + fr : 0) * p.lda;
-  const float* as0 = p.a_s + (av0 ? fr : 0) * p.as_rs;
-  const float* as1 = p.a_s + (av1 ? 16 + fr : 0) * p.as_rs;
+  const uint8_t* arow = p.A + (av ? fr : 0) * p.lda;
+  const float* asr = p.a_s + (av ? fr : 0) * p.as_rs;
   const float* bsr = p.b_s + (n0 / BK) * p.ldbs;
-  v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t kb0 = wave; kb0 < nk; kb0 += (int64_t)kSkinnyWaves * kSkinnyDepth) {
-    v8i bf[kSkinnyDepth], af0[kSkinnyDepth], af1[kSkinnyDepth];
-    float sa0[kSkinnyDepth], sa1[kSkinnyDepth], sb[kSkinnyDepth];
+    v8i bf[kSkinnyDepth], af[kSkinnyDepth];
+    float sa[kSkinnyDepth], sb[kSkinnyDepth];
 #pragma unroll
     for (int d = 0; d < kSkinnyDepth; ++d) {
       const int64_t kb = kb0 + (int64_t)d * kSkinnyWaves;
       const bool live = kb < nk;
       const int64_t k = kb * BK + 32 * fg;
-      bf[d] = skinny_frag<true>(brow, bv && live, k, K);
-      af0[d] = skinny_frag<false>(arow0, av0 && live, k, K);
-      af1[d] = skinny_frag<false>(arow1, av1 && live, k, K);
-      sa0[d] = live && av0 ? as0[kb * p.as_ks] : 0.0f;
-      sa1[d] = live && av1 ? as1[kb * p.as_ks] : 0.0f;
+      bf[d] = skinny_frag(brow, bv && live, k, K);
+      af[d] = skinny_frag(arow, av && live, k, K);
+      sa[d] = live && av ? asr[kb * p.as_ks] : 0.0f;
       sb[d] = live ? bsr[kb] : 0.0f;
     }
 #pragma unroll
     for (int d = 0; d < kSkinnyDepth; ++d) {
       if (kb0 + (int64_t)d * kSkinnyWaves >= nk) break;
       if constexpr (POW2) {
-        // rows past M carry scale 0 here, which the MFMA reads as 2^-127
+        // a row past M carries scale 0 here, which the MFMA reads as 2^-127
         // times a zero fragment: still zero
-        const int eb = (int)(__float_as_uint(sb[d]) >> 23);
-        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af0[d], acc0, 0, 0, 0, eb, 0,
-                                                                (int)(__float_as_uint(sa0[d]) >> 23));
-        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af1[d], acc1, 0, 0, 0, eb, 0,
-                                                                (int)(__float_as_uint(sa1[d]) >> 23));
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af[d], acc, 0, 0, 0,
+                                                               (int)(__float_as_uint(sb[d]) >> 23), 0,
+                                                               (int)(__float_as_uint(sa[d]) >> 23));
       } else {
         const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-        const v4f p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af0[d], z, 0, 0, 0, 0, 0, 0);
-        const v4f p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af1[d], z, 0, 0, 0, 0, 0, 0);
-        const float s0 = sa0[d] * sb[d], s1 = sa1[d] * sb[d];
+        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af[d], z, 0, 0, 0, 0, 0, 0);
+        const float sc = sa[d] * sb[d];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          acc0[v] = __builtin_fmaf(p0[v], s0, acc0[v]);
-          acc1[v] = __builtin_fmaf(p1[v], s1, acc1[v]);
-        }
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(part[v], sc, acc[v]);
       }
     }
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    red[wave][0][lane][v] = acc0[v];
-    red[wave][1][lane][v] = acc1[v];
-  }
+  for (int v = 0; v < 4; ++v) red[wave][lane][v] = acc[v];
   __syncthreads();
-  // Thread t < 512 finishes output (row t / 16, column t % 16).
+  // Thread t < 256 finishes output (row t / 16, column t % 16).
   const int t = threadIdx.x;
-  if (t >= 512) return;
+  if (t >= kSkinnyRows * 16) return;
   const int r = t >> 4, c = t & 15;
-  const int i = r >> 4, l = (c >> 2) * 16 + (r & 15), v = c & 3;
+  const int l = (c >> 2) * 16 + r, v = c & 3;
   float sum = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSkinnyWaves; ++w) sum += red[w][i][l][v];
+  for (int w = 0; w < kSkinnyWaves; ++w) sum += red[w][l][v];
   if (r < p.M && n0 + c < p.N) p.C[(int64_t)r * p.ldc + n0 + c] = __builtin_bit_cast(uint16_t, (__bf16)sum);
 }
 
@@ -1069,11 +1052,10 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmArgs p) {
 // One workgroup per (row tile of an expert, column tile).  The grid is sized
 // for the worst case; the real number of row tiles is ts[E].  Ids past the
 // real work exit at once; the rest are renumbered XCD-contiguously over the
-// real work, column tile fastest, so an expert's rows are fetched once per
-// XCD and reused across its column tiles, and consecutive row tiles of a
-// large expert share each weight tile in L2.  pid is the workgroup's index
-// within its launch range, which starts at a multiple of 8 (so pid % 8 is
-// still its XCD).
+// real work, expert by expert, so the concurrent tiles of an XCD share the
+// expert's activation rows and weight panels in its L2.  pid is the
+// workgroup's index within its launch range, which starts at a multiple of 8
+// (so pid % 8 is still its XCD).
 template <class CF, int VEC, bool GLU>
 __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uint8_t* smem) {
   const int32_t* ts = p.tile_start;
@@ -1252,7 +1234,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // 16-column workgroup re-reads twice the weight's bytes of activations
 // (32 x 36864 x 7168: 112 vs 65 us).
 bool skinny_ok(const GemmArgs& a) {
-  return a.M <= 16 && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) &&
+  return a.M <= kSkinnyRows && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) &&
          aligned(a.B, 16);
 }
 
