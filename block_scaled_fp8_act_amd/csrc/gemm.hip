@@ -1229,8 +1229,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 // The skinny kernel loads 16-byte chunks of A and B rows.  Measured against
-// the tiled kernels it is faster up to 16 rows (1 x 18432 x 7168: 33 vs 52 us;
-// 16 x 7168 x 2048: 8.7 vs 12.1 us) and not beyond: at 32 rows every
+// the tiled kernels it is faster up to 16 rows (1 x 18432 x 7168: 29 vs 52 us;
+// 16 x 7168 x 2048: 8.0 vs 12.1 us) and not beyond: at 32 rows every
 // 16-column workgroup re-reads twice the weight's bytes of activations
 // (32 x 36864 x 7168: 112 vs 65 us).
 bool skinny_ok(const GemmArgs& a) {
