@@ -638,6 +638,8 @@ def main():
         others["decode_qa"] = bench_small_gemm(dev, 50, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True)
         others["ragged_ue8m0"] = bench_small_gemm(dev, 50, "ragged ue8m0: 333x2500x1000", 333, 2500, 1000,
                                                   "ue8m0", False)
+        others["decode_one_token"] = bench_small_gemm(dev, 20, "one-token decode of the dense FFN's w1: 1x18432x7168",
+                                                      1, 18432, 7168, "fp32", False)
         line["other_workloads"] = others
     if not args.quick and not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
