@@ -136,6 +136,55 @@ def run_dense(st, steps, warmup):
     return s0.elapsed_time(s1) / steps, T
 
 
+class NoTimer:
+    """Stand-in for Timer inside graph capture (no events in the graph)."""
+
+    def run(self, name, fn):
+        fn()
+
+
+def capture(step_fn):
+    """One step captured into a HIP graph (the step only enqueues device work)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_fn()
+    return g
+
+
+def _bits(t):
+    return t.contiguous().view(-1).view(torch.uint8)
+
+
+def check_replays(g, eager_step, outs, replays=3):
+    """Replay the graph `replays` times with the eager step in between; every
+    replay must reproduce the eager step's outputs bit for bit."""
+    for _ in range(replays):
+        eager_step()
+        torch.cuda.synchronize()
+        want = [o.clone() for o in outs]
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            if not torch.equal(_bits(o), _bits(w)):
+                raise RuntimeError("graph replay differs from the eager step")
+
+
+def time_graph(g, steps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        g.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    return s0.elapsed_time(s1) / steps
+
+
 def dense_kernels(st, T):
     M, D, F = st["M"], st["D"], st["F"]
     k = {}
@@ -271,15 +320,15 @@ def bench_moe(dev, iters):
     yr = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
     y = torch.empty((Tk, D), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(lib.dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
     T = Timer()
 
     def route():
+        stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.dsfp8_moe_route(idx.data_ptr(), Tk, k, k, E, offd.data_ptr(), row_token.data_ptr(),
                                  token_rows.data_ptr(), rws.data_ptr(), rws.numel(), stream)
         assert st == 0, st
 
-    def step():
+    def step(T=T):
         T.run("route", route)
         T.run("act_quant_rows", lambda: ds.act_quant_rows(x, row_token, out=(xq, xs)))
         T.run("grouped_up_gate",
@@ -318,7 +367,12 @@ def bench_moe(dev, iters):
         res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                      "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
     res["route"] = {"us": round(T.avg_us("route"), 1)}
-    res["step_us"] = round(s0.elapsed_time(s1) * 1e3 / iters, 1)
+    res["step_us_eager"] = round(s0.elapsed_time(s1) * 1e3 / iters, 1)
+    g = capture(lambda: step(NoTimer()))
+    check_replays(g, lambda: step(NoTimer()), [offd, row_token, token_rows, xq, xs, hq, hs, yr, y])
+    res["step_us"] = round(time_graph(g, iters, 2) * 1e3, 1)
+    res["step_timing"] = "one captured HIP graph per step, replayed back to back"
+    del g
     del q13, q2
     return res
 
@@ -585,7 +639,13 @@ def main():
     props = torch.cuda.get_device_properties(dev)
 
     st = setup_dense(dev)
-    step_ms, T = run_dense(st, args.steps, args.warmup)
+    eager_ms, T = run_dense(st, args.steps, args.warmup)
+    # The step as one captured graph (same kernels, no host launch gaps),
+    # checked against the eager step before it is timed.
+    g = capture(lambda: dense_step(st, NoTimer()))
+    b = st["b"]
+    check_replays(g, lambda: dense_step(st, NoTimer()), [b[n] for n in ("xq", "xs", "hq", "hs", "out")])
+    step_ms = time_graph(g, args.steps, args.warmup)
 
     M, D, F = st["M"], st["D"], st["F"]
     fl_up, fl_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
@@ -603,6 +663,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
+        "ms_per_step_eager": round(eager_ms, 4),
+        "step_timing": "one captured HIP graph per step, replayed back to back (eager launches: ms_per_step_eager)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
