@@ -679,17 +679,34 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
     // and share one activation scale.  Row-subtile i's MFMAs are issued
     // before the rescale of row-subtile i-1, so the fma of a partial product
     // never waits for the MFMA that has just produced it.
+    // Row-subtile i+1's activation fragment and scale are read before
+    // subtile i's MFMAs (in program order ahead of the inline-asm load
+    // issues, which the compiler does not move memory reads across), so the
+    // LDS latency is covered by a subtile's MFMAs instead of stalling the
+    // first MFMA of every subtile.
+    auto ascale = [&](int i) __attribute__((always_inline)) {
+      return sl[(i * 16 / CF::SA_ROWS) * CF::SAW + (i * 16) % CF::SA_ROWS];
+    };
+    v8i afr = frag(at);
+    float asv = ascale(0);
     if constexpr (POW2) {
       const int eb = (int)(__float_as_uint(bsv) >> 23);
 #pragma unroll
       for (int i = 0; i < CF::TM; ++i) {
-        const v8i afr = frag(at + i * 16 * BK);
-        const int ea = (int)(__float_as_uint(sl[(i * 16 / CF::SA_ROWS) * CF::SAW + (i * 16) % CF::SA_ROWS]) >> 23);
+        v8i afr_next = afr;
+        float asv_next = asv;
+        if (i + 1 < CF::TM) {
+          afr_next = frag(at + (i + 1) * 16 * BK);
+          asv_next = ascale(i + 1);
+        }
+        const int ea = (int)(__float_as_uint(asv) >> 23);
 #pragma unroll
         for (int j = 0; j < CF::TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, acc[i][j], 0, 0, 0, eb, 0, ea);
 #pragma unroll
         for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+        afr = afr_next;
+        asv = asv_next;
       }
       continue;
     }
@@ -698,12 +715,19 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 #pragma unroll
     for (int i = 0; i <= CF::TM; ++i) {
       if (i < CF::TM) {
-        const v8i afr = frag(at + i * 16 * BK);
-        scv[i & 1] = sl[(i * 16 / CF::SA_ROWS) * CF::SAW + (i * 16) % CF::SA_ROWS] * bsv;
+        v8i afr_next = afr;
+        float asv_next = asv;
+        if (i + 1 < CF::TM) {
+          afr_next = frag(at + (i + 1) * 16 * BK);
+          asv_next = ascale(i + 1);
+        }
+        scv[i & 1] = asv * bsv;
 #pragma unroll
         for (int j = 0; j < CF::TN; ++j)
           part[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+        afr = afr_next;
+        asv = asv_next;
 #pragma unroll
         for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
       }
