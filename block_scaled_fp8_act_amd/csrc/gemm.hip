@@ -599,10 +599,9 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
   // Load n (0 .. LOADS-1) of K-block kb into `stage`: n < A_INSTR are A
-  // segments, then B segments, then the scale gather.  Callers issuing past
-  // the last K-block pass the last one again (into a stage nobody reads), so
-  // no branch is needed.  Chunks past K (only in a last, partial K-block) go
-  // to an offset beyond the descriptor and read as zero.
+  // segments, then B segments, then the scale gather.  Chunks past K (only
+  // in a last, partial K-block) go to an offset beyond the descriptor and
+  // read as zero.
   auto issue_one = [&](int n, int kb, int stage) __attribute__((always_inline)) {
     const uint32_t st = lds0 + (uint32_t)(stage * CF::STAGE_BYTES);
     const uint32_t kbyte = (uint32_t)kb * BK;
@@ -663,7 +662,10 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
     const int later = (kb1 - 1 - kb) < (CF::STAGES - 2) ? (kb1 - 1 - kb) : (CF::STAGES - 2);
     wait_stage<CF>(later);
     __syncthreads();
-    const int kn = kb + CF::STAGES - 1 < kb1 ? kb + CF::STAGES - 1 : kb1 - 1;
+    // The last STAGES - 1 K-blocks issue no loads (a uniform branch): loads
+    // past the end would only delay the epilogue, which waits for all of them.
+    const bool more = kb + CF::STAGES - 1 < kb1;
+    const int kn = more ? kb + CF::STAGES - 1 : kb1 - 1;
     const int slot = (kb - kb0 + CF::STAGES - 1) % CF::STAGES;
     const uint8_t* st = smem + ((kb - kb0) % CF::STAGES) * CF::STAGE_BYTES;
     const float* sarea = reinterpret_cast<const float*>(st + CF::S_OFF);
@@ -703,8 +705,10 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 #pragma unroll
         for (int j = 0; j < CF::TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, acc[i][j], 0, 0, 0, eb, 0, ea);
+        if (more) {
 #pragma unroll
-        for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+          for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+        }
         afr = afr_next;
         asv = asv_next;
       }
@@ -728,8 +732,10 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
               bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
         afr = afr_next;
         asv = asv_next;
+        if (more) {
 #pragma unroll
-        for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+          for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+        }
       }
       if (i > 0) {
         const int r = i - 1;
