@@ -61,9 +61,9 @@ def _mat(t, name, dtypes, dim=2):
     if t.dtype not in dtypes:
         raise Dsfp8Error(f"{name} must have dtype in {dtypes}, got {t.dtype}")
     if t.dim() != dim:
-        raise Dsfp8Error(f"Input tensors must have {dim} dimensions ({name} has {t.dim()})")
+        raise Dsfp8Error(f"{name} must be {dim}-D, got {t.dim()} dimensions")
     if t.numel() > 0 and t.stride(-1) != 1:
-        raise Dsfp8Error(f"Input tensor must be contiguous in its last dimension ({name})")
+        raise Dsfp8Error(f"{name}: the last dimension needs stride 1")
     return t
 
 
@@ -225,7 +225,7 @@ def grouped_gemm(a, a_s, b, b_s, offsets, out=None, workspace=None, scale_fmt="f
     if K2 != K or offsets.numel() != E + 1:
         raise Dsfp8Error("shape mismatch between a, b and offsets")
     if not b.is_contiguous() or not b_s.is_contiguous():
-        raise Dsfp8Error("Input tensor must be contiguous (b, b_s)")
+        raise Dsfp8Error("b and b_s need contiguous storage")
     if tuple(b_s.shape) != (E, kblocks(N), kblocks(K)) or tuple(a_s.shape) != (M, kblocks(K)):
         raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and b_s [E, ceil(N/128), ceil(K/128)]")
     lib = _lib.load()
@@ -293,7 +293,7 @@ def grouped_gemm_silu_mul_act_quant(a, a_s, w13, w13_s, offsets, scale_fmt="fp32
     if K2 != K or N2 % 2 or offsets.numel() != E + 1:
         raise Dsfp8Error("shape mismatch between a, w13 and offsets")
     if not w.is_contiguous() or not w13_s.is_contiguous():
-        raise Dsfp8Error("Input tensor must be contiguous (w13, w13_s)")
+        raise Dsfp8Error("w13 and w13_s need contiguous storage")
     F = N2 // 2
     if tuple(w13_s.shape) != (E, kblocks(N2), kblocks(K)) or tuple(a_s.shape) != (M, kblocks(K)):
         raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and w13_s [E, 2F/128, ceil(K/128)]")
@@ -337,7 +337,7 @@ def _int32_mat(t, name):
     if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or t.dim() != 2:
         raise Dsfp8Error(f"{name} must be a 2-D int32 CUDA tensor")
     if t.numel() > 0 and t.stride(-1) != 1:
-        raise Dsfp8Error(f"Input tensor must be contiguous in its last dimension ({name})")
+        raise Dsfp8Error(f"{name}: the last dimension needs stride 1")
     return t
 
 

@@ -26,7 +26,7 @@ What it computes, and where the pages define it:
   order of the (token, slot) pairs, the gathered act_quant and the weighted
   bf16 combine (Admin Guide 6.4 and 8.4).
 
-Precision: the pages fix fp32 for the quantisers ("load ... as float32"), so
+Precision: the pages fix fp32 for the quantisers (the data are converted to fp32 first), so
 those run in IEEE binary32 through NumPy float32 scalars/arrays, whose
 arithmetic is correctly rounded.  The products are formed in fp64.
 

@@ -11,10 +11,10 @@
 * ``weight_dequant`` -- Admin Guide 8.5.2 ``weight_dequant_kernel``.
 
 All arithmetic is IEEE binary32 (NumPy float32, correctly rounded), because
-the pages load the data "as float32" before taking the maximum, dividing and
+the pages convert the data to fp32 before taking the maximum, dividing and
 multiplying.
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
 
 * the clamp is applied to the block's absolute maximum before the division by
   448 (the pages' order: absolute max, clamp to 1e-4, divide by 448), and the
