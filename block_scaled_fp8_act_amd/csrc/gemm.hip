@@ -473,26 +473,27 @@ struct DmaCfg {
 };
 
 // Large products: 256x256 tiles, 8 waves of 128x64 (one workgroup per CU);
-// products with too few of those tiles, split-K products and the grouped
-// form's 65-128-row class: 128x128 tiles, 4 waves of 64x64 (two workgroups
-// per CU).
+// products with too few of those tiles and split-K products: 128x128 tiles,
+// 4 waves of 64x64 (two workgroups per CU).
 #ifndef DSFP8_DMA_TILE
 #define DSFP8_DMA_TILE 256, 256, 2, 4, 2
 #endif
 using CfgDmaBig = DmaCfg<DSFP8_DMA_TILE>;
 using CfgDma = DmaCfg<128, 128, 2, 2, 2>;
-// Grouped form's class of at most 64 rows, and dense products of 17 to 64
-// rows: 64-row tiles, 4 waves of 64x32.
+// Dense products of 17 to 64 rows (and their split-K form): 64-row tiles,
+// 4 waves of 64x32.
 #ifndef DSFP8_GROUPED_TILE
 #define DSFP8_GROUPED_TILE 64, 128, 1, 4, 2
 #endif
 using CfgGrp = DmaCfg<DSFP8_GROUPED_TILE>;
-// Gated form: 256-column tiles (128 columns of each half), 8 waves of 32x64
-// or 64x64 for small row counts; the large dense tile otherwise.  The small
-// tiles take 83 KB and 100 KB of LDS per stage pair, so one workgroup fits
-// per CU; a third stage (125 KB, 149 KB) keeps more weight bytes in flight,
-// which measured 8% faster on the routed-expert up-projection, whose small
-// experts stream their weights once.
+// Gated form, and the grouped classes of at most 64 and 65-128 rows of both
+// forms: 256-column tiles (for the gated form 128 columns of each half),
+// 8 waves of 32x64 or 64x64; the large dense tile otherwise.  The small tiles
+// take 83 KB and 100 KB of LDS per stage pair, so one workgroup fits per CU;
+// a third stage (125 KB, 149 KB) keeps more weight bytes in flight, which
+// measured 8% faster on the routed-expert up-projection, whose small experts
+// stream their weights once.  With all three classes at 8 waves, a grouped
+// product runs them in one launch (grouped_merged_kernel).
 #ifndef DSFP8_GLU64_TILE
 #define DSFP8_GLU64_TILE 64, 256, 2, 4, 3
 #endif
@@ -1139,15 +1140,15 @@ __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) 
   grouped_tile<CF, VEC, GLU>(p, blockIdx.x, smem);
 }
 
-// The three tile classes of the gated grouped product in one launch: ids
-// [0, n2) run class 2 (the tallest tiles, which take longest), then n1 ids of
-// class 1, then class 0, so the short tiles fill the CUs that the tall ones
-// leave idle at the end instead of waiting for a launch of their own.  All
-// three use 8 waves and one workgroup per CU (their LDS rings take 125 to
-// 149 KB), so sharing one kernel costs no occupancy.  n2 and n1 are
-// multiples of 8.  p holds the class-0 schedule; class c's is c*(E+1) later.
-template <class C0, class C1, class C2, int VEC>
-__global__ __launch_bounds__(C2::kThreads) void grouped_glu_kernel(GemmArgs p, int64_t n2, int64_t n1) {
+// The three tile classes of a grouped product in one launch: ids [0, n2) run
+// class 2 (the tallest tiles, which take longest), then n1 ids of class 1,
+// then class 0, so the short tiles fill the CUs that the tall ones leave idle
+// at the end instead of waiting for a launch of their own.  All three use 8
+// waves and one workgroup per CU (their LDS rings take 125 to 149 KB), so
+// sharing one kernel costs no occupancy.  n2 and n1 are multiples of 8.  p
+// holds the class-0 schedule; class c's is c*(E+1) later.
+template <class C0, class C1, class C2, int VEC, bool GLU>
+__global__ __launch_bounds__(C2::kThreads) void grouped_merged_kernel(GemmArgs p, int64_t n2, int64_t n1) {
   static_assert(C0::kThreads == C2::kThreads && C1::kThreads == C2::kThreads, "one workgroup size");
   constexpr int L01 = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
   constexpr int LDS = L01 > C2::LDS_BYTES ? L01 : C2::LDS_BYTES;
@@ -1157,14 +1158,14 @@ __global__ __launch_bounds__(C2::kThreads) void grouped_glu_kernel(GemmArgs p, i
   if (id < n2) {
     q.grp_class = 2;
     q.tile_start = p.tile_start + 2 * (p.E + 1);
-    grouped_tile<C2, VEC, true>(q, id, smem);
+    grouped_tile<C2, VEC, GLU>(q, id, smem);
   } else if (id < n2 + n1) {
     q.grp_class = 1;
     q.tile_start = p.tile_start + (p.E + 1);
-    grouped_tile<C1, VEC, true>(q, id - n2, smem);
+    grouped_tile<C1, VEC, GLU>(q, id - n2, smem);
   } else {
     q.grp_class = 0;
-    grouped_tile<C0, VEC, true>(q, id - n2 - n1, smem);
+    grouped_tile<C0, VEC, GLU>(q, id - n2 - n1, smem);
   }
 }
 
@@ -1341,31 +1342,24 @@ hipError_t grouped_classes(const GemmArgs& a, hipStream_t stream) {
   c2.tile_start = a.tile_start + 2 * (E + 1);
   const int64_t s0 = mn(E, M), s1 = mn(E, M / (C0::BM + 1));
   const int64_t s2 = (M + C2::BM - 1) / C2::BM + mn(E, M / (C1::BM + 1));
-  if constexpr (GLU) {
-    auto up8 = [](int64_t v) { return (v + 7) / 8 * 8; };
-    const int64_t n2 = up8(s2 * tiles_n(C2::BN)), n1 = up8(s1 * tiles_n(C1::BN)), n0 = s0 * tiles_n(C0::BN);
-    const dim3 grid((unsigned)(n2 + n1 + n0)), blk(C2::kThreads);
-    const bool kfull = a.K % BK == 0;
-    if (a.pow2) {
-      if (kfull) hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, -2>), grid, blk, 0, stream, c0, n2, n1);
-      else hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, -3>), grid, blk, 0, stream, c0, n2, n1);
-    } else {
-      if (kfull) hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, 0>), grid, blk, 0, stream, c0, n2, n1);
-      else hipLaunchKernelGGL((grouped_glu_kernel<C0, C1, C2, -1>), grid, blk, 0, stream, c0, n2, n1);
-    }
-    return hipGetLastError();
+  auto up8 = [](int64_t v) { return (v + 7) / 8 * 8; };
+  const int64_t n2 = up8(s2 * tiles_n(C2::BN)), n1 = up8(s1 * tiles_n(C1::BN)), n0 = s0 * tiles_n(C0::BN);
+  const dim3 grid((unsigned)(n2 + n1 + n0)), blk(C2::kThreads);
+  const bool kfull = a.K % BK == 0;
+  if (a.pow2) {
+    if (kfull) hipLaunchKernelGGL((grouped_merged_kernel<C0, C1, C2, -2, GLU>), grid, blk, 0, stream, c0, n2, n1);
+    else hipLaunchKernelGGL((grouped_merged_kernel<C0, C1, C2, -3, GLU>), grid, blk, 0, stream, c0, n2, n1);
   } else {
-    if (s0 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C0, GLU, dim3((unsigned)(s0 * tiles_n(C0::BN))), stream, c0);
-    if (s1 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C1, GLU, dim3((unsigned)(s1 * tiles_n(C1::BN))), stream, c1);
-    if (s2 > 0) DSFP8_LAUNCH_DMA(grouped_gemm_kernel, C2, GLU, dim3((unsigned)(s2 * tiles_n(C2::BN))), stream, c2);
-    return hipGetLastError();
+    if (kfull) hipLaunchKernelGGL((grouped_merged_kernel<C0, C1, C2, 0, GLU>), grid, blk, 0, stream, c0, n2, n1);
+    else hipLaunchKernelGGL((grouped_merged_kernel<C0, C1, C2, -1, GLU>), grid, blk, 0, stream, c0, n2, n1);
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.M == 0) return hipSuccess;
-  if (pick_vec<CfgGrp>(a) <= 0 && pick_vec<CfgDma>(a) <= 0 && pick_vec<CfgDmaBig>(a) <= 0)
-    return grouped_classes<CfgGrp, CfgDma, CfgDmaBig, false>(a, stream);
+  if (pick_vec<CfgGlu64>(a) <= 0 && pick_vec<CfgGlu128>(a) <= 0 && pick_vec<CfgDmaBig>(a) <= 0)
+    return grouped_classes<CfgGlu64, CfgGlu128, CfgDmaBig, false>(a, stream);
   static_assert(CfgDma::BM == Cfg128::BM, "one tile height for both pipelines");
   GemmArgs s = a;
   s.grp_class = 0;
