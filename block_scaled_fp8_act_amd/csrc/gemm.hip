@@ -155,10 +155,13 @@ __device__ __forceinline__ void stage_c(const v4f (&acc)[CF::TM][CF::TN], uint8_
     }
 }
 
-// Epilogue: stage the tile in LDS, then write rows of C with 16-byte stores.
-template <class CF, bool COLS>
+// Epilogue: stage the tile in LDS, read each lane's rows of it into
+// registers, call hook() (which may wait for those reads and reuse the LDS),
+// then write rows of C with 16-byte stores.
+template <class CF, bool COLS, class Hook>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, const v4f (&acc)[CF::TM][CF::TN],
-                                           uint8_t* smem, int wave, int wm, int wn, int lane) {
+                                           uint8_t* smem, int wave, int wm, int wn, int lane, Hook&& hook) {
+  asm volatile("" : "+v"(lane));
   const int64_t N = p.N;
   constexpr int CS = CF::WN + CF::CPAD;
   const uint16_t* cst = reinterpret_cast<const uint16_t*>(smem) + wave * CF::WM * CS;
@@ -169,23 +172,31 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, 
   const int64_t row_lim = t.row_end;
   const bool cvec = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 8 == 0);
   constexpr int CPR = CF::WN / 8;  // 16-byte chunks per staged row
+  constexpr int IT = CF::WM * CPR / 64;
+  u32x4 v[IT];
 #pragma unroll
-  for (int it = 0; it < CF::WM * CPR / 64; ++it) {
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane + 64 * it;
+    v[it] = *reinterpret_cast<const u32x4*>(cst + (c / CPR) * CS + (c % CPR) * 8);
+  }
+  hook();
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
     const int c = lane + 64 * it;
     const int r = c / CPR, cc = c % CPR;
     const int64_t row = crow0 + r;
     const int64_t col = ccol0 + cc * 8;
     if (row >= row_lim || col >= N) continue;
-    const uint16_t* src = cst + r * CS + cc * 8;
     uint16_t* dst = p.C + row * p.ldc + col;
     if (cvec && col + 8 <= N) {
 #ifdef DSFP8_NT_STORE
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst));
 #else
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      *reinterpret_cast<u32x4*>(dst) = v[it];
 #endif
     } else {
-      for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = src[e];
+      const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+      for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -326,7 +337,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
     store_partial<CF, false>(p, t, acc, wm, wn, lane);
     return;
   }
-  store_tile<CF, false>(p, t, acc, smem, wave, wm, wn, lane);
+  store_tile<CF, false>(p, t, acc, smem, wave, wm, wn, lane, [] {});
 }
 
 // Gated epilogue ("DeepSeek-V3 Administrator & Developer Guide" 1.2, the
@@ -337,10 +348,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileRef& t, u
 // lanes takes one tile row, 8 outputs per lane: h = bf16(SiLU(h1) * h3), the
 // block maximum over the 16 lanes, then the block's scale and e4m3 codes,
 // computed exactly as the standalone gate-and-quantise kernel does.
-template <class CF>
+template <class CF, class Hook>
 __device__ __forceinline__ void store_glu_quant(const GemmArgs& p, const TileRef& t,
                                                 const v4f (&acc)[CF::TM][CF::TN], uint8_t* smem, int wave,
-                                                int lane) {
+                                                int lane, Hook&& hook) {
+  asm volatile("" : "+v"(lane));
   static_assert(CF::BN == 2 * kBlock && kBlock % CF::WN == 0, "one 128-column block of each half per tile");
   static_assert(CF::BM % (4 * CF::NW) == 0, "whole groups of four rows per wave");
   stage_c<CF, true>(acc, smem, wave, lane);
@@ -353,12 +365,21 @@ __device__ __forceinline__ void store_glu_quant(const GemmArgs& p, const TileRef
   // w3 column in wave column (128 + c) / WN; both at column c % WN there.
   const int wc1 = c / CF::WN, wc3 = (kBlock + c) / CF::WN, cc = c % CF::WN;
   const int64_t blk = t.n0 / kBlock;
+  // All of this lane's staged values are read first, so hook() may reuse the LDS.
+  constexpr int IT = CF::BM / (4 * CF::NW);
+  u32x4 gs[IT], us[IT];
 #pragma unroll
-  for (int it = 0; it < CF::BM / (4 * CF::NW); ++it) {
+  for (int it = 0; it < IT; ++it) {
     const int r = (it * CF::NW + wave) * 4 + quad;
     const int rw = r / CF::WM, rr = r % CF::WM;
-    const u32x4 g = *reinterpret_cast<const u32x4*>(cst + ((rw * CF::WAVES_N + wc1) * CF::WM + rr) * CS + cc);
-    const u32x4 u = *reinterpret_cast<const u32x4*>(cst + ((rw * CF::WAVES_N + wc3) * CF::WM + rr) * CS + cc);
+    gs[it] = *reinterpret_cast<const u32x4*>(cst + ((rw * CF::WAVES_N + wc1) * CF::WM + rr) * CS + cc);
+    us[it] = *reinterpret_cast<const u32x4*>(cst + ((rw * CF::WAVES_N + wc3) * CF::WM + rr) * CS + cc);
+  }
+  hook();
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int r = (it * CF::NW + wave) * 4 + quad;
+    const u32x4 g = gs[it], u = us[it];
     const float gv[8] = {bf16_lo(g.x), bf16_hi(g.x), bf16_lo(g.y), bf16_hi(g.y),
                          bf16_lo(g.z), bf16_hi(g.z), bf16_lo(g.w), bf16_hi(g.w)};
     const float uv[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
@@ -439,6 +460,15 @@ __device__ __forceinline__ void dma_gather_b32(uint32_t lds, const float* addr) 
                : "memory");
 }
 
+// The lane index behind an empty statement: values derived from it are
+// computed where they are used instead of being hoisted out of a persistent
+// kernel's tile loop, where they would stay live across the K loop.
+__device__ __forceinline__ int lane_id() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 constexpr uint32_t kOob = 0x80000000u;  // above every descriptor's size
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -475,6 +505,10 @@ struct DmaCfg {
 // Large products: 256x256 tiles, 8 waves of 128x64 (one workgroup per CU);
 // products with too few of those tiles and split-K products: 128x128 tiles,
 // 4 waves of 64x64 (two workgroups per CU).
+// Large dense products run as one persistent workgroup per CU.
+#ifndef DSFP8_PERSISTENT
+#define DSFP8_PERSISTENT 1
+#endif
 #ifndef DSFP8_DMA_TILE
 #define DSFP8_DMA_TILE 256, 256, 2, 4, 2
 #endif
@@ -544,94 +578,135 @@ __device__ __forceinline__ void wait_stage(int later) {
 // GLU: the gated form (BN = 256): the tile's weight rows are w1 rows
 // n0..n0+127 followed by w3 rows F+n0..F+n0+127, and the epilogue is the
 // gate and quantisation instead of the bf16 store.
-template <class CF, bool KFULL, bool POW2, bool GLU>
-__device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
-  constexpr int NW = CF::NW;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
-  const int64_t K = p.K, N = p.N;
-  const int64_t kbn = (N + BK - 1) / BK;
-
-  const int64_t rowsA = t.row_end - t.row0 < CF::BM ? t.row_end - t.row0 : CF::BM;
-  const i32x4 rsA = make_rsrc(t.A + t.row0 * p.lda, (uint32_t)(rowsA * p.lda));
-  // The weight-scale row of this wave's 128-column block (clamped for waves
-  // past the last column, whose results are never stored).
-  int64_t nbi;
-  i32x4 rsB;
-  if constexpr (GLU) {
-    static_assert(CF::BN == 2 * BK, "gated tiles hold one 128-row block of w1 and of w3");
-    // One descriptor from w1 row n0 to the end of w3 row F + n0 + 127.
-    rsB = make_rsrc(t.B + t.n0 * p.ldb, (uint32_t)((p.glu_f + BK) * p.ldb));
-    nbi = (wn * CF::WN < BK ? 0 : p.glu_f / BK) + t.n0 / BK;
-  } else {
-    const int64_t rowsB = N - t.n0 < CF::BN ? N - t.n0 : CF::BN;
-    rsB = make_rsrc(t.B + t.n0 * p.ldb, (uint32_t)(rowsB * p.ldb));
-    nbi = (t.n0 + wn * CF::WN) / BK;
-    if (nbi > kbn - 1) nbi = kbn - 1;
-  }
-  // Scale gather: lane l < SA_ROWS fetches a_s of tile row wave*SA_ROWS + l,
-  // lane SA_ROWS fetches b_s[nbi, kb]; K-block kb adds kb * sstep bytes.
-  const int srow = wave * CF::SA_ROWS + lane;
-  const bool s_act = lane < CF::SA_ROWS ? srow < rowsA : lane == CF::SA_ROWS;
-  const float* sbase = lane < CF::SA_ROWS ? t.a_s + (t.row0 + srow) * p.as_rs : t.b_s + nbi * p.ldbs;
-  const uint32_t sstep = lane < CF::SA_ROWS ? (uint32_t)(p.as_ks * 4) : 4u;
-
-  // Per-lane source offsets (K-block independent): lane -> LDS chunk (row r,
-  // physical chunk lane % 8) <- logical chunk c of row r.
+// Per-wave state of the direct-to-LDS loads of one tile: the buffer
+// descriptors of the tile's A rows and B rows, the per-lane source offsets of
+// the wave's segments and the address of its scale gather.  Re-initialised
+// for every tile.
+template <class CF, bool KFULL, bool GLU>
+struct DmaLoader {
+  i32x4 rsA, rsB;
   uint32_t offA[CF::A_INSTR], offB[CF::B_INSTR];
-  int kcA[CF::A_INSTR], kcB[CF::B_INSTR];
+  // Logical 16-byte chunk (0..7) of segment n's lane at bits 4n..4n+2
+  // (A segments, then B segments); only read for a K-block with chunks past K.
+  uint32_t kc;
+  const float* sbase;
+  uint32_t sstep;
+  bool s_act;
+  int64_t K;
+  uint32_t lds0;
+  int wave;
+
+  __device__ __forceinline__ void init(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
+    constexpr int NW = CF::NW;
+    const int lane = lane_id();
+    wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wn = wave % CF::WAVES_N;
+    K = p.K;
+    const int64_t N = p.N;
+    const int64_t kbn = (N + BK - 1) / BK;
+    const int64_t rowsA = t.row_end - t.row0 < CF::BM ? t.row_end - t.row0 : CF::BM;
+    rsA = make_rsrc(t.A + t.row0 * p.lda, (uint32_t)(rowsA * p.lda));
+    // The weight-scale row of this wave's 128-column block (clamped for waves
+    // past the last column, whose results are never stored).
+    int64_t nbi;
+    if constexpr (GLU) {
+      static_assert(CF::BN == 2 * BK, "gated tiles hold one 128-row block of w1 and of w3");
+      // One descriptor from w1 row n0 to the end of w3 row F + n0 + 127.
+      rsB = make_rsrc(t.B + t.n0 * p.ldb, (uint32_t)((p.glu_f + BK) * p.ldb));
+      nbi = (wn * CF::WN < BK ? 0 : p.glu_f / BK) + t.n0 / BK;
+    } else {
+      const int64_t rowsB = N - t.n0 < CF::BN ? N - t.n0 : CF::BN;
+      rsB = make_rsrc(t.B + t.n0 * p.ldb, (uint32_t)(rowsB * p.ldb));
+      nbi = (t.n0 + wn * CF::WN) / BK;
+      if (nbi > kbn - 1) nbi = kbn - 1;
+    }
+    // Scale gather: lane l < SA_ROWS fetches a_s of tile row wave*SA_ROWS + l,
+    // lane SA_ROWS fetches b_s[nbi, kb]; K-block kb adds kb * sstep bytes.
+    const int srow = wave * CF::SA_ROWS + lane;
+    s_act = lane < CF::SA_ROWS ? srow < rowsA : lane == CF::SA_ROWS;
+    sbase = lane < CF::SA_ROWS ? t.a_s + (t.row0 + srow) * p.as_rs : t.b_s + nbi * p.ldbs;
+    sstep = lane < CF::SA_ROWS ? (uint32_t)(p.as_ks * 4) : 4u;
+    // Per-lane source offsets (K-block independent): lane -> LDS chunk (row
+    // r, physical chunk lane % 8) <- logical chunk c of row r.
+    static_assert(CF::A_INSTR + CF::B_INSTR <= 8, "chunk indices packed in 32 bits");
+    kc = 0;
 #pragma unroll
-  for (int i = 0; i < CF::A_INSTR; ++i) {
-    const int r = (wave + NW * i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_key(r);
-    offA[i] = (uint32_t)(r * p.lda + c * 16);
-    kcA[i] = c * 16;
-  }
+    for (int i = 0; i < CF::A_INSTR; ++i) {
+      const int r = (wave + NW * i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz_key(r);
+      offA[i] = (uint32_t)(r * p.lda + c * 16);
+      kc |= (uint32_t)c << (4 * i);
+    }
 #pragma unroll
-  for (int i = 0; i < CF::B_INSTR; ++i) {
-    const int r = (wave + NW * i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_key(r);
-    const int64_t rb = (GLU && r >= BK) ? p.glu_f + (r - BK) : (int64_t)r;  // row past the descriptor base
-    offB[i] = (uint32_t)(rb * p.ldb + c * 16);
-    kcB[i] = c * 16;
+    for (int i = 0; i < CF::B_INSTR; ++i) {
+      const int r = (wave + NW * i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz_key(r);
+      const int64_t rb = (GLU && r >= BK) ? p.glu_f + (r - BK) : (int64_t)r;  // row past the descriptor base
+      offB[i] = (uint32_t)(rb * p.ldb + c * 16);
+      kc |= (uint32_t)c << (4 * (CF::A_INSTR + i));
+    }
+    lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
   }
 
-  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
   // Load n (0 .. LOADS-1) of K-block kb into `stage`: n < A_INSTR are A
   // segments, then B segments, then the scale gather.  Chunks past K (only
   // in a last, partial K-block) go to an offset beyond the descriptor and
   // read as zero.
-  auto issue_one = [&](int n, int kb, int stage) __attribute__((always_inline)) {
+  __device__ __forceinline__ void issue(int n, int kb, int stage) const {
+    constexpr int NW = CF::NW;
     const uint32_t st = lds0 + (uint32_t)(stage * CF::STAGE_BYTES);
     const uint32_t kbyte = (uint32_t)kb * BK;
+    const int64_t kchunk = (int64_t)kbyte + (int64_t)(((kc >> (4 * n)) & 7u) * 16u);
     if (n < CF::A_INSTR) {
-      const uint32_t off = (KFULL || (int64_t)kbyte + kcA[n] < K) ? offA[n] : kOob;
+      const uint32_t off = (KFULL || kchunk < K) ? offA[n] : kOob;
       dma_b128(rsA, st + (uint32_t)((wave + NW * n) * 1024), off, kbyte);
     } else if (n < CF::A_INSTR + CF::B_INSTR) {
       const int m = n - CF::A_INSTR;
-      const uint32_t off = (KFULL || (int64_t)kbyte + kcB[m] < K) ? offB[m] : kOob;
+      const uint32_t off = (KFULL || kchunk < K) ? offB[m] : kOob;
       dma_b128(rsB, st + (uint32_t)(CF::A_BYTES + (wave + NW * m) * 1024), off, kbyte);
     } else if (s_act) {
       const float* src = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(sbase) +
                                                         (uint64_t)(uint32_t)kb * sstep);
       dma_gather_b32(st + (uint32_t)(CF::S_OFF + wave * CF::SAW * 4), src);
     }
-  };
+  }
 
-  v4f acc[CF::TM][CF::TN];
+  // K-blocks kb0 .. kb0 + n - 1 (at most kb1 - 1) into stages 0 .. n - 1.
+  __device__ __forceinline__ void preload(int kb0, int kb1, int n) const {
+    for (int s = 0; s < n; ++s)
+      if (kb0 + s < kb1)
+#pragma unroll
+        for (int i = 0; i < CF::LOADS; ++i) issue(i, kb0 + s, s);
+  }
+};
+
+// The K loop of one tile over K-blocks [kb0, kb1) into acc.  K-blocks kb0 ..
+// kb0 + pre - 1 were issued into stages 0 .. pre - 1 before the call (pre is
+// STAGES - 1, or STAGES when the previous tile's epilogue issued them);
+// K-block kb + STAGES - 1 is issued during K-block kb unless it already was.
+// first_all: the first wait covers every outstanding vector-memory operation
+// (required when pre = STAGES, and when the previous tile's stores may still
+// be in flight: loads and stores need not complete in order).
+//
+// KFULL: K is a multiple of 128, so no K-block has chunks past K.
+// POW2: every scale is a power of two.  The block-scaled form of the MFMA
+// then applies them: with the operand layout used here, lane l supplies the
+// E8M0 scale (the fp32 exponent field, value 2^(e-127)) of operand row l % 16
+// for the 32-byte K slice l / 16, and a 128-K-block's four slices share
+// their scale, so each lane passes its own row's exponent and the MFMA
+// accumulates straight into the accumulator.  (Without POW2 the scale
+// operands are the literal 0, for which the compiler emits the unscaled
+// instruction; a zero scale supplied at run time would mean 2^-127.)
+template <class CF, bool KFULL, bool POW2, bool GLU>
+__device__ __forceinline__ void k_loop(const DmaLoader<CF, KFULL, GLU>& ld, int kb0, int kb1, int pre, bool first_all,
+                                       uint8_t* smem, v4f (&acc)[CF::TM][CF::TN]) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
 #pragma unroll
   for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
     for (int j = 0; j < CF::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int kb0 = t.kb0, kb1 = t.kb1;
-#pragma unroll
-  for (int s = 0; s < CF::STAGES - 1; ++s)
-    if (kb0 + s < kb1)
-#pragma unroll
-      for (int n = 0; n < CF::LOADS; ++n) issue_one(n, kb0 + s, s);
 
   // Fragment addressing.  Row R + fr of an operand tile (R a multiple of 16)
   // keeps its logical chunk c at fr*128 + ((c ^ key(fr)) << 4) past row R, so
@@ -660,13 +735,18 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
   // instruction issue until the load unit has accepted them.
   constexpr int PER = (CF::LOADS + CF::TM - 1) / CF::TM;
   for (int kb = kb0; kb < kb1; ++kb) {
-    const int later = (kb1 - 1 - kb) < (CF::STAGES - 2) ? (kb1 - 1 - kb) : (CF::STAGES - 2);
-    wait_stage<CF>(later);
+    if (first_all && kb == kb0) {
+      wait_vmcnt<0>();
+    } else {
+      const int later = (kb1 - 1 - kb) < (CF::STAGES - 2) ? (kb1 - 1 - kb) : (CF::STAGES - 2);
+      wait_stage<CF>(later);
+    }
     __syncthreads();
-    // The last STAGES - 1 K-blocks issue no loads (a uniform branch): loads
-    // past the end would only delay the epilogue, which waits for all of them.
-    const bool more = kb + CF::STAGES - 1 < kb1;
-    const int kn = more ? kb + CF::STAGES - 1 : kb1 - 1;
+    // K-block kn is issued now unless it was issued before the loop or lies
+    // past the end (a uniform branch: the last STAGES - 1 K-blocks issue
+    // nothing).
+    const int kn = kb + CF::STAGES - 1;
+    const bool more = kn < kb1 && kn >= kb0 + pre;
     const int slot = (kb - kb0 + CF::STAGES - 1) % CF::STAGES;
     const uint8_t* st = smem + ((kb - kb0) % CF::STAGES) * CF::STAGE_BYTES;
     const float* sarea = reinterpret_cast<const float*>(st + CF::S_OFF);
@@ -708,7 +788,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, acc[i][j], 0, 0, 0, eb, 0, ea);
         if (more) {
 #pragma unroll
-          for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+          for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) ld.issue(n, kn, slot);
         }
         afr = afr_next;
         asv = asv_next;
@@ -735,7 +815,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
         asv = asv_next;
         if (more) {
 #pragma unroll
-          for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) issue_one(n, kn, slot);
+          for (int n = i * PER; n < (i + 1) * PER && n < CF::LOADS; ++n) ld.issue(n, kn, slot);
         }
       }
       if (i > 0) {
@@ -753,18 +833,36 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
       }
     }
   }
-  // Loads issued for K-blocks past the end must land before the LDS is reused.
+}
+
+// One tile by itself: preload STAGES - 1 K-blocks, the K loop, the epilogue.
+// GLU: the gated form (BN = 256): the tile's weight rows are w1 rows
+// n0..n0+127 followed by w3 rows F+n0..F+n0+127, and the epilogue is the
+// gate and quantisation instead of the bf16 store.
+template <class CF, bool KFULL, bool POW2, bool GLU>
+__device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& t, uint8_t* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  DmaLoader<CF, KFULL, GLU> ld;
+  ld.init(p, t, smem);
+  ld.preload(t.kb0, t.kb1, CF::STAGES - 1);
+  v4f acc[CF::TM][CF::TN];
+  k_loop<CF, KFULL, POW2, GLU>(ld, t.kb0, t.kb1, CF::STAGES - 1, false, smem, acc);
+  // Every load has landed and every wave is done with the ring before the
+  // epilogue reuses the LDS.
   wait_vmcnt<0>();
   __syncthreads();
+  auto none = [] {};
   if constexpr (GLU) {
-    store_glu_quant<CF>(p, t, acc, smem, wave, lane);
+    store_glu_quant<CF>(p, t, acc, smem, wave, lane, none);
     return;
   }
   if (t.partial != nullptr) {
     store_partial<CF, true>(p, t, acc, wm, wn, lane);
     return;
   }
-  store_tile<CF, true>(p, t, acc, smem, wave, wm, wn, lane);
+  store_tile<CF, true>(p, t, acc, smem, wave, wm, wn, lane, none);
 }
 
 // Workgroup i runs on XCD i % 8.  Renumber ids 0..total-1 so that each XCD
@@ -843,6 +941,70 @@ __global__ __launch_bounds__(CF::kThreads) void gemm_kernel(GemmArgs p) {
     t.partial = p.partial + (int64_t)blockIdx.y * p.M * p.N;
   }
   run_tile<CF, VEC, GLU>(p, t, smem);
+}
+
+// Large dense products as a persistent kernel: one workgroup per CU walks
+// the tiles pid = blockIdx.x, + gridDim.x, ...  gridDim.x is a multiple of the
+// 8 XCDs, so all of a workgroup's tiles lie in its own XCD's range and the
+// tiles in flight together are the ones a launch of one workgroup per tile
+// would run together.  The next tile's first STAGES K-blocks are issued from
+// the epilogue as soon as the staged results have been read back from LDS,
+// so their latency is covered by the epilogue's arithmetic and stores.
+template <class CF, int VEC, bool GLU = false>
+__global__ __launch_bounds__(CF::kThreads) void gemm_persistent_kernel(GemmArgs p) {
+  static_assert(VEC <= 0, "direct-to-LDS pipeline only");
+  constexpr bool KFULL = VEC == 0 || VEC == -2, POW2 = VEC <= -2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
+  const int64_t tiles_m = (p.M + CF::BM - 1) / CF::BM;
+  const int64_t tiles_n = col_tiles<CF, GLU>(p);
+  const int64_t total = tiles_m * tiles_n;
+  const int kb1 = (int)((p.K + BK - 1) / BK);
+  const int pre = kb1 < CF::STAGES ? kb1 : CF::STAGES;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  auto tile = [&](int64_t pid) __attribute__((always_inline)) {
+    int64_t tm, tn;
+    tile_of(pid, tiles_m, tiles_n, tm, tn);
+    TileRef r;
+    r.A = p.A;
+    r.a_s = p.a_s;
+    r.B = p.B;
+    r.b_s = p.b_s;
+    r.row0 = tm * CF::BM;
+    r.row_end = p.M;
+    r.n0 = tn * kColStep<CF, GLU>;
+    r.kb0 = 0;
+    r.kb1 = kb1;
+    r.partial = nullptr;
+    return r;
+  };
+  int64_t pid = blockIdx.x;
+  TileRef t = tile(pid);
+  DmaLoader<CF, KFULL, GLU> ld;
+  ld.init(p, t, smem);
+  ld.preload(0, kb1, pre);
+  v4f acc[CF::TM][CF::TN];
+  for (;;) {
+    k_loop<CF, KFULL, POW2, GLU>(ld, 0, kb1, pre, true, smem, acc);
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int64_t next = pid + gridDim.x;
+    auto prefetch = [&]() __attribute__((always_inline)) {
+      __syncthreads();  // every wave has read its staged results
+      if (next < total) {
+        ld.init(p, tile(next), smem);
+        ld.preload(0, kb1, pre);
+      }
+    };
+    if constexpr (GLU)
+      store_glu_quant<CF>(p, t, acc, smem, wave, lane, prefetch);
+    else
+      store_tile<CF, true>(p, t, acc, smem, wave, wm, wn, lane, prefetch);
+    if (next >= total) break;
+    pid = next;
+    t = tile(pid);
+  }
 }
 
 // Sum the split-K partials in split order (deterministic) and round to bf16.
@@ -1303,7 +1465,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) <= 0) {
+#if DSFP8_PERSISTENT
+    DSFP8_LAUNCH_DMA(gemm_persistent_kernel, CfgDmaBig, false, dim3((unsigned)device_cu_count()), stream, a);
+#else
     DSFP8_LAUNCH_DMA(gemm_kernel, CfgDmaBig, false, dense_grid<CfgDmaBig>(a), stream, a);
+#endif
     return hipGetLastError();
   }
   if (a.M <= CfgGrp::BM && pick_vec<CfgGrp>(a) <= 0) {
@@ -1390,7 +1556,11 @@ hipError_t launch_gemm_glu(const GemmArgs& a, hipStream_t stream) {
   auto grid = [&](int bm) { return dim3((unsigned)(((a.M + bm - 1) / bm) * nt)); };
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * nt;
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count())
+#if DSFP8_PERSISTENT
+    DSFP8_LAUNCH_DMA(gemm_persistent_kernel, CfgDmaBig, true, dim3((unsigned)device_cu_count()), stream, a);
+#else
     DSFP8_LAUNCH_DMA(gemm_kernel, CfgDmaBig, true, grid(CfgDmaBig::BM), stream, a);
+#endif
   else if (a.M > CfgGlu64::BM)
     DSFP8_LAUNCH_DMA(gemm_kernel, CfgGlu128, true, grid(CfgGlu128::BM), stream, a);
   else
