@@ -313,8 +313,8 @@ def bench_moe(dev, iters):
     row_token = torch.empty(M, dtype=torch.int32, device=dev)
     token_rows = torch.empty((Tk, k), dtype=torch.int32, device=dev)
     rws = torch.empty(lib.dsfp8_moe_route_workspace_bytes(Tk, k, E), dtype=torch.uint8, device=dev)
-    xq = torch.empty((M, D), dtype=torch.uint8, device=dev)
-    xs = ds.new_scales(M, kb(D), dev)
+    xq = torch.empty((Tk, D), dtype=torch.uint8, device=dev)
+    xs = ds.new_scales(Tk, kb(D), dev)
     hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
     hs = ds.new_scales(M, kb(F), dev)
     yr = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
@@ -330,9 +330,12 @@ def bench_moe(dev, iters):
 
     def step(T=T):
         T.run("route", route)
-        T.run("act_quant_rows", lambda: ds.act_quant_rows(x, row_token, out=(xq, xs)))
+        # The token rows are quantised once; the up-projection reads each
+        # expert row through row_token.
+        T.run("act_quant", lambda: ds.act_quant(x, out=(xq, xs)))
         T.run("grouped_up_gate",
-              lambda: ds.grouped_gemm_silu_mul_act_quant(xq, xs, q13, s13, offd, out=(hq, hs), workspace=ws))
+              lambda: ds.grouped_gemm_silu_mul_act_quant(xq, xs, q13, s13, offd, out=(hq, hs), workspace=ws,
+                                                         rows=row_token))
         T.run("grouped_down", lambda: ds.grouped_gemm(hq, hs, q2, s2, offd, out=yr, workspace=ws))
         T.run("combine", lambda: ds.moe_combine(yr, idx, wts, token_rows, out=y))
 
@@ -360,9 +363,9 @@ def bench_moe(dev, iters):
         roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
         res[name] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
                      "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3)}
-    # act_quant_rows reads the routed rows of x (2 B), writes e4m3 and scales;
+    # act_quant reads the token rows of x (2 B), writes e4m3 and scales;
     # combine reads the expert outputs and writes the token outputs (bf16).
-    for name, by in (("act_quant_rows", aq_bytes(M, D)), ("combine", 2 * M * D + 2 * Tk * D + Tk * k * 10)):
+    for name, by in (("act_quant", aq_bytes(Tk, D)), ("combine", 2 * M * D + 2 * Tk * D + Tk * k * 10)):
         us = T.avg_us(name)
         res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                      "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}

@@ -278,36 +278,49 @@ def gemm_silu_mul_act_quant(a, a_s, w13, w13_s, scale_fmt="fp32", return_h=False
 
 
 def grouped_gemm_silu_mul_act_quant(a, a_s, w13, w13_s, offsets, scale_fmt="fp32", return_h=False, out=None,
-                                    workspace=None):
+                                    workspace=None, rows=None):
     """Grouped form of :func:`gemm_silu_mul_act_quant`: rows
     ``offsets[e]:offsets[e+1]`` of A use expert e's stacked ``w13[e]`` e4m3
-    ``[2F, K]`` and ``w13_s[e]`` ``[2F/128, ceil(K/128)]``."""
+    ``[2F, K]`` and ``w13_s[e]`` ``[2F/128, ceil(K/128)]``.
+
+    ``rows`` (int32 CUDA tensor [M_total], optional): product row r reads row
+    ``rows[r]`` of ``a`` and ``a_s`` (clamped to ``[0, a.shape[0])``), so the
+    per-token quantised input feeds the experts without a gathered copy."""
     a = _mat(_bytes(a), "a", (torch.uint8,))
     w = _mat(_bytes(w13), "w13", (torch.uint8,), dim=3)
     ars, aks = _scale_matrix(a_s, "a_s")
     _mat(w13_s, "w13_s", (torch.float32,), dim=3)
     if not offsets.is_cuda or offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
         raise Dsfp8Error("offsets must be a contiguous int32 CUDA tensor of length E+1")
-    M, K = a.shape
+    A_rows, K = a.shape
+    if rows is not None:
+        if not rows.is_cuda or rows.dtype != torch.int32 or rows.dim() != 1 or not rows.is_contiguous():
+            raise Dsfp8Error("rows must be a contiguous 1-D int32 CUDA tensor")
+        M = rows.numel()
+    else:
+        M = A_rows
     E, N2, K2 = w.shape
     if K2 != K or N2 % 2 or offsets.numel() != E + 1:
         raise Dsfp8Error("shape mismatch between a, w13 and offsets")
     if not w.is_contiguous() or not w13_s.is_contiguous():
         raise Dsfp8Error("w13 and w13_s need contiguous storage")
     F = N2 // 2
-    if tuple(w13_s.shape) != (E, kblocks(N2), kblocks(K)) or tuple(a_s.shape) != (M, kblocks(K)):
-        raise Dsfp8Error("scale shapes must be a_s [M, ceil(K/128)] and w13_s [E, 2F/128, ceil(K/128)]")
+    if tuple(w13_s.shape) != (E, kblocks(N2), kblocks(K)) or tuple(a_s.shape) != (A_rows, kblocks(K)):
+        raise Dsfp8Error("scale shapes must be a_s [rows of a, ceil(K/128)] and w13_s [E, 2F/128, ceil(K/128)]")
     lib = _lib.load()
     y, s, h = _glu_outputs(M, F, a.device, out, return_h)
     srs, sks = _scale_strides(s)
     wsb = lib.dsfp8_grouped_gemm_workspace_bytes(E, M, N2, K)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
-    st = lib.dsfp8_grouped_gemm_silu_mul_act_quant(
-        a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, w.data_ptr(), K, w13_s.data_ptr(), kblocks(K),
-        offsets.data_ptr(), E, M, F, K, y.data_ptr(), _ld(y), s.data_ptr(), srs, sks,
-        h.data_ptr() if h is not None else None, F, _fmt(scale_fmt), workspace.data_ptr(), workspace.numel(),
-        _stream(a))
+    tail = (w.data_ptr(), K, w13_s.data_ptr(), kblocks(K), offsets.data_ptr(), E, M, F, K, y.data_ptr(), _ld(y),
+            s.data_ptr(), srs, sks, h.data_ptr() if h is not None else None, F, _fmt(scale_fmt),
+            workspace.data_ptr(), workspace.numel(), _stream(a))
+    if rows is None:
+        st = lib.dsfp8_grouped_gemm_silu_mul_act_quant(a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, *tail)
+    else:
+        st = lib.dsfp8_grouped_gemm_silu_mul_act_quant_gather(a.data_ptr(), A_rows, _ld(a), a_s.data_ptr(), ars,
+                                                              aks, rows.data_ptr(), *tail)
     _check("grouped_gemm_silu_mul_act_quant", st)
     return (y, s, h) if return_h else (y, s)
 

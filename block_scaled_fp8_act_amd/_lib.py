@@ -30,6 +30,9 @@ SIGNATURES = {
     "dsfp8_grouped_gemm_silu_mul_act_quant": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64,
                                                    _i64, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i, _p, _sz,
                                                    _p]),
+    "dsfp8_grouped_gemm_silu_mul_act_quant_gather": (_i, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _i64, _p, _i64,
+                                                          _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _p,
+                                                          _i64, _i, _p, _sz, _p]),
     "dsfp8_act_quant_rows": (_i, [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i, _p]),
     "dsfp8_moe_route": (_i, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "dsfp8_moe_route_workspace_bytes": (_sz, [_i64, _i64, _i64]),

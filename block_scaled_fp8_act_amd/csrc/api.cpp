@@ -286,14 +286,14 @@ namespace {
 
 // Arguments of the gated product, checked as the product and the quantiser
 // check theirs; E experts of 2F weight rows each (E = 1: the dense form).
-dsfp8_status glu_args(const void* A, int64_t lda, const float* a_s, int64_t as_rs, int64_t as_ks, const void* W13,
-                      int64_t ldw, const float* w_s, int64_t ldws, int64_t E, int64_t M, int64_t F, int64_t K,
-                      void* y, int64_t ldy, float* s, int64_t s_rs, int64_t s_ks, void* h, int64_t ldh,
+dsfp8_status glu_args(const void* A, int64_t a_rows, int64_t lda, const float* a_s, int64_t as_rs, int64_t as_ks,
+                      const void* W13, int64_t ldw, const float* w_s, int64_t ldws, int64_t E, int64_t M, int64_t F,
+                      int64_t K, void* y, int64_t ldy, float* s, int64_t s_rs, int64_t s_ks, void* h, int64_t ldh,
                       int scale_fmt, dsfp8::GemmArgs& a) {
-  if (!dim_ok(M) || !dim_ok(F) || !dim_ok(K) || !dim_ok(2 * F)) return DSFP8_ERR_SHAPE;
+  if (!dim_ok(M) || !dim_ok(F) || !dim_ok(K) || !dim_ok(2 * F) || !dim_ok(a_rows)) return DSFP8_ERR_SHAPE;
   if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
-  DSFP8_TRY(check_mat(A, M, K, lda, 1));
-  DSFP8_TRY(check_scales(a_s, M, nblk(K), as_rs, as_ks));
+  DSFP8_TRY(check_mat(A, a_rows, K, lda, 1));
+  DSFP8_TRY(check_scales(a_s, a_rows, nblk(K), as_rs, as_ks));
   DSFP8_TRY(check_mat(W13, E * 2 * F, K, ldw, 1));
   DSFP8_TRY(check_mat(w_s, E * nblk(2 * F), nblk(K), ldws, 4));
   DSFP8_TRY(check_quant_out(M, F, y, ldy, s, s_rs, s_ks));
@@ -327,13 +327,47 @@ dsfp8_status glu_args(const void* A, int64_t lda, const float* a_s, int64_t as_r
 
 }  // namespace
 
+namespace {
+
+// The grouped gated product, with A's rows read directly (rows == NULL,
+// a_rows == M_total) or through the index rows.
+dsfp8_status grouped_glu(const void* A, int64_t a_rows, int64_t lda, const float* a_s, int64_t as_rs, int64_t as_ks,
+                         const int32_t* rows, const void* W13, int64_t ldw, const float* w_s, int64_t ldws,
+                         const int32_t* offsets, int64_t E, int64_t M_total, int64_t F, int64_t K, void* y,
+                         int64_t ldy, float* s, int64_t s_rs, int64_t s_ks, void* h, int64_t ldh, int scale_fmt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
+  if (offsets == nullptr) return DSFP8_ERR_NULL;
+  if (!al(offsets, 4)) return DSFP8_ERR_ALIGN;
+  dsfp8::GemmArgs a;
+  DSFP8_TRY(glu_args(A, a_rows, lda, a_s, as_rs, as_ks, W13, ldw, w_s, ldws, E, M_total, F, K, y, ldy, s, s_rs, s_ks,
+                     h, ldh, scale_fmt, a));
+  const size_t need = dsfp8_grouped_gemm_workspace_bytes(E, M_total, 2 * F, K);
+  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
+  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
+  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
+  if (rows != nullptr) {
+    // one buffer descriptor spans every row of A (32-bit offsets)
+    if (a_rows * lda + K >= ((int64_t)1 << 31)) return DSFP8_ERR_UNSUPPORTED;
+    a.a_rows = rows;
+    a.a_rows_n = a_rows;
+  }
+  if (M_total == 0 || F == 0) return DSFP8_OK;
+  a.offsets = offsets;
+  a.E = E;
+  a.tile_start = static_cast<int32_t*>(workspace);
+  return launched(dsfp8::launch_grouped_gemm_glu(a, stream));
+}
+
+}  // namespace
+
 dsfp8_status dsfp8_gemm_silu_mul_act_quant(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
                                            int64_t as_kb_stride, const void* W13, int64_t ldw, const float* w_s,
                                            int64_t ldws, int64_t M, int64_t F, int64_t K, void* y, int64_t ldy,
                                            float* s, int64_t s_row_stride, int64_t s_kb_stride, void* h,
                                            int64_t ldh, int scale_fmt, hipStream_t stream) {
   dsfp8::GemmArgs a;
-  DSFP8_TRY(glu_args(A, lda, a_s, as_row_stride, as_kb_stride, W13, ldw, w_s, ldws, 1, M, F, K, y, ldy, s,
+  DSFP8_TRY(glu_args(A, M, lda, a_s, as_row_stride, as_kb_stride, W13, ldw, w_s, ldws, 1, M, F, K, y, ldy, s,
                      s_row_stride, s_kb_stride, h, ldh, scale_fmt, a));
   if (M == 0 || F == 0) return DSFP8_OK;
   return launched(dsfp8::launch_gemm_glu(a, stream));
@@ -346,21 +380,27 @@ dsfp8_status dsfp8_grouped_gemm_silu_mul_act_quant(const void* A, int64_t lda, c
                                                    int64_t K, void* y, int64_t ldy, float* s, int64_t s_row_stride,
                                                    int64_t s_kb_stride, void* h, int64_t ldh, int scale_fmt,
                                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
-  if (offsets == nullptr) return DSFP8_ERR_NULL;
-  if (!al(offsets, 4)) return DSFP8_ERR_ALIGN;
-  dsfp8::GemmArgs a;
-  DSFP8_TRY(glu_args(A, lda, a_s, as_row_stride, as_kb_stride, W13, ldw, w_s, ldws, E, M_total, F, K, y, ldy, s,
-                     s_row_stride, s_kb_stride, h, ldh, scale_fmt, a));
-  const size_t need = dsfp8_grouped_gemm_workspace_bytes(E, M_total, 2 * F, K);
-  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
-  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
-  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
-  if (M_total == 0 || F == 0) return DSFP8_OK;
-  a.offsets = offsets;
-  a.E = E;
-  a.tile_start = static_cast<int32_t*>(workspace);
-  return launched(dsfp8::launch_grouped_gemm_glu(a, stream));
+  return grouped_glu(A, M_total, lda, a_s, as_row_stride, as_kb_stride, nullptr, W13, ldw, w_s, ldws, offsets, E,
+                     M_total, F, K, y, ldy, s, s_row_stride, s_kb_stride, h, ldh, scale_fmt, workspace,
+                     workspace_bytes, stream);
+}
+
+dsfp8_status dsfp8_grouped_gemm_silu_mul_act_quant_gather(const void* A, int64_t a_rows, int64_t lda,
+                                                          const float* a_s, int64_t as_row_stride,
+                                                          int64_t as_kb_stride, const int32_t* rows,
+                                                          const void* W13, int64_t ldw, const float* w_s,
+                                                          int64_t ldws, const int32_t* offsets, int64_t E,
+                                                          int64_t M_total, int64_t F, int64_t K, void* y,
+                                                          int64_t ldy, float* s, int64_t s_row_stride,
+                                                          int64_t s_kb_stride, void* h, int64_t ldh, int scale_fmt,
+                                                          void* workspace, size_t workspace_bytes,
+                                                          hipStream_t stream) {
+  if (M_total > 0 && rows == nullptr) return DSFP8_ERR_NULL;
+  if (!al(rows, 4)) return DSFP8_ERR_ALIGN;
+  if (M_total > 0 && a_rows < 1) return DSFP8_ERR_SHAPE;
+  return grouped_glu(A, a_rows, lda, a_s, as_row_stride, as_kb_stride, rows, W13, ldw, w_s, ldws, offsets, E,
+                     M_total, F, K, y, ldy, s, s_row_stride, s_kb_stride, h, ldh, scale_fmt, workspace,
+                     workspace_bytes, stream);
 }
 
 dsfp8_status dsfp8_act_quant_rows(const void* x, int64_t x_rows, int64_t ldx, const int32_t* rows, int64_t M,

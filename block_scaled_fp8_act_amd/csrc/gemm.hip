@@ -619,7 +619,15 @@ struct DmaLoader {
     const int64_t N = p.N;
     const int64_t kbn = (N + BK - 1) / BK;
     const int64_t rowsA = t.row_end - t.row0 < CF::BM ? t.row_end - t.row0 : CF::BM;
-    rsA = make_rsrc(t.A + t.row0 * p.lda, (uint32_t)(rowsA * p.lda));
+    // Gathered rows: one descriptor over all of A, each lane's source row
+    // from the index (clamped); rows past the tile's end read as zero.
+    const bool gather = p.a_rows != nullptr;
+    auto src_row = [&](int r) __attribute__((always_inline)) {
+      int64_t v = p.a_rows[t.row0 + r];
+      return v < 0 ? (int64_t)0 : (v >= p.a_rows_n ? p.a_rows_n - 1 : v);
+    };
+    rsA = gather ? make_rsrc(t.A, (uint32_t)(p.a_rows_n * p.lda))
+                 : make_rsrc(t.A + t.row0 * p.lda, (uint32_t)(rowsA * p.lda));
     // The weight-scale row of this wave's 128-column block (clamped for waves
     // past the last column, whose results are never stored).
     int64_t nbi;
@@ -638,7 +646,8 @@ struct DmaLoader {
     // lane SA_ROWS fetches b_s[nbi, kb]; K-block kb adds kb * sstep bytes.
     const int srow = wave * CF::SA_ROWS + lane;
     s_act = lane < CF::SA_ROWS ? srow < rowsA : lane == CF::SA_ROWS;
-    sbase = lane < CF::SA_ROWS ? t.a_s + (t.row0 + srow) * p.as_rs : t.b_s + nbi * p.ldbs;
+    const int64_t arow = !s_act || lane >= CF::SA_ROWS ? 0 : (gather ? src_row(srow) : t.row0 + srow);
+    sbase = lane < CF::SA_ROWS ? t.a_s + arow * p.as_rs : t.b_s + nbi * p.ldbs;
     sstep = lane < CF::SA_ROWS ? (uint32_t)(p.as_ks * 4) : 4u;
     // Per-lane source offsets (K-block independent): lane -> LDS chunk (row
     // r, physical chunk lane % 8) <- logical chunk c of row r.
@@ -648,7 +657,8 @@ struct DmaLoader {
     for (int i = 0; i < CF::A_INSTR; ++i) {
       const int r = (wave + NW * i) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz_key(r);
-      offA[i] = (uint32_t)(r * p.lda + c * 16);
+      offA[i] = !gather ? (uint32_t)(r * p.lda + c * 16)
+                        : (r < rowsA ? (uint32_t)(src_row(r) * p.lda + c * 16) : kOob);
       kc |= (uint32_t)c << (4 * i);
     }
 #pragma unroll

@@ -101,6 +101,10 @@ struct GemmArgs {
   float* partial;
   // every scale is a power of two: the MFMA applies them (exponents only)
   bool pow2;
+  // grouped gated form: product row r reads row a_rows[r] of A and a_s
+  // (clamped to [0, a_rows_n)); NULL: row r itself
+  const int32_t* a_rows;
+  int64_t a_rows_n;
   // gated form: B stacks w1 (rows 0..F-1) over w3 (rows F..2F-1), N = 2F; the
   // epilogue computes h = bf16(SiLU(bf16(x w1^T)) * bf16(x w3^T)) and writes
   // act_quant(h) as e4m3 qy [M, F] and fp32 scales qs (element (m, b) at

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSFP8_ABI_VERSION 4
+#define DSFP8_ABI_VERSION 5
 #define DSFP8_BLOCK 128
 
 typedef int dsfp8_status;
@@ -298,6 +298,33 @@ dsfp8_status dsfp8_grouped_gemm_silu_mul_act_quant(const void* A, int64_t lda,
                                                    float* s, int64_t s_row_stride, int64_t s_kb_stride,
                                                    void* h, int64_t ldh, int scale_fmt,
                                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsfp8_grouped_gemm_silu_mul_act_quant with the activation rows read through
+ * an index, so the per-token quantised input feeds the experts without a
+ * gathered copy ([AG] 6.4 / 8.4: expert e's input is x[idx]; the per-row,
+ * per-128-column quantisation of 8.5.1 commutes with that row selection):
+ * row r of the product is row rows[r] of A, with its scales.
+ *
+ *   A      e4m3 [a_rows, K], row stride lda                 (device, read)
+ *   a_s    fp32 [a_rows, KB(K)], strides as for dsfp8_gemm  (device, read)
+ *   rows   int32 [M_total]; each entry is clamped to [0, a_rows) (device, read)
+ * All other arguments as for dsfp8_grouped_gemm_silu_mul_act_quant (y, s, h
+ * have M_total rows, in product-row order).  Also required: a_rows >= 1
+ * when M_total > 0, and a_rows * lda + K < 2^31 (else UNSUPPORTED).
+ * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, WORKSPACE, UNSUPPORTED, LAUNCH.
+ */
+dsfp8_status dsfp8_grouped_gemm_silu_mul_act_quant_gather(const void* A, int64_t a_rows, int64_t lda,
+                                                          const float* a_s, int64_t as_row_stride,
+                                                          int64_t as_kb_stride, const int32_t* rows,
+                                                          const void* W13, int64_t ldw, const float* w_s,
+                                                          int64_t ldws, const int32_t* offsets, int64_t E,
+                                                          int64_t M_total, int64_t F, int64_t K,
+                                                          void* y, int64_t ldy,
+                                                          float* s, int64_t s_row_stride, int64_t s_kb_stride,
+                                                          void* h, int64_t ldh, int scale_fmt,
+                                                          void* workspace, size_t workspace_bytes,
+                                                          hipStream_t stream);
 
 /*
  * act_quant of gathered rows: the expert inputs x[idx] of [AG] 6.4 / 8.4

@@ -257,3 +257,33 @@ def test_grouped_gated_product_validation(lib):
     assert call(ws=None) == NULL
     assert call(F=200, ldy=200) == UNSUP
     assert call(M=0) == OK
+
+
+def test_grouped_gated_gather_validation(lib):
+    g = lib.dsfp8_grouped_gemm_silu_mul_act_quant_gather
+    names = ["A", "a_rows", "lda", "a_s", "as_rs", "as_ks", "rows", "W", "ldw", "w_s", "ldws", "offsets", "E", "M",
+             "F", "K", "y", "ldy", "s", "srs", "sks", "h", "ldh", "fmt", "ws", "wsb", "stream"]
+    args = [P, 40, 256, P, 1, 40, P, P, 256, P, 2, P, 4, 100, 256, 256, P, 256, P, 1, 100, None, 0, 0, P, 1 << 20,
+            None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return g(*a)
+
+    assert call(rows=None) == NULL
+    assert call(rows=P + 2) == ALIGN
+    assert call(a_rows=0) == SHAPE
+    assert call(a_rows=-1) == SHAPE
+    assert call(lda=100) == LD                # lda below K
+    assert call(E=0) == SHAPE
+    assert call(offsets=None) == NULL
+    assert call(fmt=7) == FMT
+    assert call(wsb=0) == WS
+    assert call(F=200, ldy=200) == UNSUP
+    # one descriptor spans all of A: a_rows * lda + K must stay below 2^31
+    assert call(a_rows=(1 << 31) // 256, as_ks=(1 << 31) // 256, lda=256) == UNSUP
+    # no rows: nothing to do, nothing launched (the pointers are never touched)
+    assert call(M=0) == OK
+    assert call(M=0, rows=None) == OK

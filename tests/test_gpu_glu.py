@@ -42,7 +42,7 @@ from oracle import glue
 from oracle import moe
 from oracle import quant as Q
 
-from gpu_helpers import dev_f32, dev_scales, dev_u8, host_bits16, host_f32_bits, host_u8
+from gpu_helpers import dev_bf16, dev_f32, dev_scales, dev_u8, host_bits16, host_f32_bits, host_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -343,6 +343,12 @@ def test_routed_expert_size_sampled():
     h13 = ds.grouped_gemm(a, a_s, w, w_s, offd)
     assert_same(fused, ds.silu_mul_act_quant(h13[:, :F_], h13[:, F_:], return_h=True), "routed-expert size")
     del h13
+    # The per-token quantised input read through the row index gives the same
+    # bytes (act_quant is row-local, so it commutes with the row selection).
+    xq, xs = ds.act_quant(x)
+    gathered = ds.grouped_gemm_silu_mul_act_quant(xq, xs, w, w_s, offd, return_h=True, rows=rt)
+    assert_same(gathered, fused, "routed-expert size, rows read through the index")
+    del gathered
     y, s, h = fused
     counts = np.diff(offsets)
     picks = [int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30))),
@@ -363,3 +369,28 @@ def test_routed_expert_size_sampled():
         cols = slice(blk * 128, (blk + 1) * 128)
         check_against_oracle(host_u8(y[rd, cols]), s[rd, blk:blk + 1].cpu().numpy(), host_bits16(h[rd, cols]),
                              ar, asr, wq, wsq, False, f"expert {e} ({hi - lo} rows) block {blk}")
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_grouped_gather_equals_gathered_copy(fmt):
+    """Rows read through an index (with entries outside [0, T), which clamp)
+    equal the product of the explicitly gathered, quantised rows."""
+    counts = GROUP_COUNTS
+    M, F_, K, T = sum(counts), 256, 640, 300
+    g = np.random.default_rng(12)
+    x = dev_bf16(I.activations((T, K), I.MOE, 70))
+    idx = g.integers(0, T, M).astype(np.int32)
+    idx[[0, 7, M - 1]] = [-3, T + 5, T - 1]
+    rows = torch.from_numpy(idx).cuda()
+    _, _, w, w_s = rand_operands(8, F_, K, E=len(counts), ue8m0=fmt == "ue8m0", seed=13)
+    wd, wsd = dev_u8(w), dev_f32(w_s)
+    offd = torch.from_numpy(np.r_[0, np.cumsum(counts)].astype(np.int32)).cuda()
+    a, a_s = ds.act_quant_rows(x, rows, fmt)
+    ref = ds.grouped_gemm_silu_mul_act_quant(a, a_s, wd, wsd, offd, fmt, return_h=True)
+    xq, xs = ds.act_quant(x, fmt)
+    got = ds.grouped_gemm_silu_mul_act_quant(xq, xs, wd, wsd, offd, fmt, return_h=True, rows=rows)
+    assert_same(got, ref, f"gathered rows {fmt}")
+    # and the row-major scale layout of the token scales
+    xs_rm = xs.contiguous()
+    got = ds.grouped_gemm_silu_mul_act_quant(xq, xs_rm, wd, wsd, offd, fmt, return_h=True, rows=rows)
+    assert_same(got, ref, f"gathered rows {fmt}, row-major scales")
