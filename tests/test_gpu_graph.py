@@ -3,7 +3,8 @@
 None of the library's kernels allocates, clears memory with a runtime memset
 or synchronises the host, so a whole step (act_quant, the gated
 up-projection, the down-projection; for the routed experts also routing,
-row gathering and combining) can be captured once and replayed.  A replay
+the up-projection reading its rows through the routing index, and
+combining) can be captured once and replayed.  A replay
 must read the buffers as they are at replay time and write exactly what the
 eager calls write.  Each test replays several times, with new inputs written
 into the captured buffers, the eager step run and the host synchronised
@@ -76,8 +77,8 @@ def test_dense_step_graph(fmt):
     q2, s2 = Q.weight_quant(w2, ue8m0=ue)
     q13d, s13d, q2d, s2d = dev_u8(q13), dev_f32(s13), dev_u8(q2), dev_f32(s2)
     x = dev_bf16(xs_host[0])
-    xq = torch.empty((M, D), dtype=torch.uint8, device="cuda")
-    xsc = ds.new_scales(M, ds.kblocks(D), "cuda")
+    xq = torch.empty((T, D), dtype=torch.uint8, device="cuda")
+    xsc = ds.new_scales(T, ds.kblocks(D), "cuda")
     hq = torch.empty((M, Fi), dtype=torch.uint8, device="cuda")
     hsc = ds.new_scales(M, ds.kblocks(Fi), "cuda")
     out = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
@@ -125,8 +126,8 @@ def test_routed_step_graph(fmt):
     row_token = torch.empty(M, dtype=torch.int32, device="cuda")
     token_rows = torch.empty((T, k), dtype=torch.int32, device="cuda")
     rws = torch.empty(max(lib.dsfp8_moe_route_workspace_bytes(T, k, E), 4), dtype=torch.uint8, device="cuda")
-    xq = torch.empty((M, D), dtype=torch.uint8, device="cuda")
-    xsc = ds.new_scales(M, ds.kblocks(D), "cuda")
+    xq = torch.empty((T, D), dtype=torch.uint8, device="cuda")
+    xsc = ds.new_scales(T, ds.kblocks(D), "cuda")
     hq = torch.empty((M, Fi), dtype=torch.uint8, device="cuda")
     hsc = ds.new_scales(M, ds.kblocks(Fi), "cuda")
     yr = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
@@ -139,8 +140,8 @@ def test_routed_step_graph(fmt):
         st = lib.dsfp8_moe_route(idx.data_ptr(), T, k, k, E, off.data_ptr(), row_token.data_ptr(),
                                  token_rows.data_ptr(), rws.data_ptr(), rws.numel(), stream)
         assert st == 0, ds.status_string(st)
-        ds.act_quant_rows(x, row_token, fmt, out=(xq, xsc))
-        ds.grouped_gemm_silu_mul_act_quant(xq, xsc, q13d, s13d, off, fmt, out=(hq, hsc), workspace=gws)
+        ds.act_quant(x, fmt, out=(xq, xsc))
+        ds.grouped_gemm_silu_mul_act_quant(xq, xsc, q13d, s13d, off, fmt, out=(hq, hsc), workspace=gws, rows=row_token)
         ds.grouped_gemm(hq, hsc, q2d, s2d, off, out=yr, workspace=gws, scale_fmt=fmt)
         ds.moe_combine(yr, idx, wts, token_rows, out=y)
 
