@@ -77,8 +77,8 @@ def test_dense_step_graph(fmt):
     q2, s2 = Q.weight_quant(w2, ue8m0=ue)
     q13d, s13d, q2d, s2d = dev_u8(q13), dev_f32(s13), dev_u8(q2), dev_f32(s2)
     x = dev_bf16(xs_host[0])
-    xq = torch.empty((T, D), dtype=torch.uint8, device="cuda")
-    xsc = ds.new_scales(T, ds.kblocks(D), "cuda")
+    xq = torch.empty((M, D), dtype=torch.uint8, device="cuda")
+    xsc = ds.new_scales(M, ds.kblocks(D), "cuda")
     hq = torch.empty((M, Fi), dtype=torch.uint8, device="cuda")
     hsc = ds.new_scales(M, ds.kblocks(Fi), "cuda")
     out = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
