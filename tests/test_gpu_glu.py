@@ -182,9 +182,11 @@ def test_integer_operands_exact(M, F_, K, fmt):
 
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
 @pytest.mark.parametrize("M,F_,K", [(1, 128, 256), (64, 256, 7168), (65, 384, 640), (200, 256, 720),
-                                    (1300, 5504, 256)])
+                                    (1300, 5504, 256), (1300, 5504, 720)])
 def test_random_operands_against_oracle(M, F_, K, fmt):
-    # (1300, 5504): 6 x 43 tiles of 256 x 256 (the large-tile pipeline)
+    # (1300, 5504): 6 x 43 = 258 tiles of 256 x 256, the persistent kernel
+    # (two workgroups take a second tile), with M and N tails; K = 720 ends
+    # in a partial K-block
     ue = fmt == "ue8m0"
     a, a_s, w, w_s = rand_operands(M, F_, K, ue8m0=ue, seed=M)
     y, s, h, dev = run_dense(a, a_s, w[0], w_s[0], fmt)
