@@ -600,7 +600,7 @@ template <class CF, bool KFULL, bool GLU>
 struct DmaLoader {
   i32x4 rsA, rsB;
   uint32_t offA[CF::A_INSTR], offB[CF::B_INSTR];
-  // Logical 16-byte chunk (0..7) of segment n's lane at bits 4n..4n+2
+  // Logical 16-byte chunk (0..7) of segment n's lane at bits 3n..3n+2
   // (A segments, then B segments); only read for a K-block with chunks past K.
   uint32_t kc;
   const float* sbase;
@@ -651,7 +651,7 @@ struct DmaLoader {
     sstep = lane < CF::SA_ROWS ? (uint32_t)(p.as_ks * 4) : 4u;
     // Per-lane source offsets (K-block independent): lane -> LDS chunk (row
     // r, physical chunk lane % 8) <- logical chunk c of row r.
-    static_assert(CF::A_INSTR + CF::B_INSTR <= 8, "chunk indices packed in 32 bits");
+    static_assert(CF::A_INSTR + CF::B_INSTR <= 10, "chunk indices packed in 32 bits");
     kc = 0;
 #pragma unroll
     for (int i = 0; i < CF::A_INSTR; ++i) {
@@ -659,7 +659,7 @@ struct DmaLoader {
       const int c = (lane & 7) ^ swz_key(r);
       offA[i] = !gather ? (uint32_t)(r * p.lda + c * 16)
                         : (r < rowsA ? (uint32_t)(src_row(r) * p.lda + c * 16) : kOob);
-      kc |= (uint32_t)c << (4 * i);
+      kc |= (uint32_t)c << (3 * i);
     }
 #pragma unroll
     for (int i = 0; i < CF::B_INSTR; ++i) {
@@ -667,7 +667,7 @@ struct DmaLoader {
       const int c = (lane & 7) ^ swz_key(r);
       const int64_t rb = (GLU && r >= BK) ? p.glu_f + (r - BK) : (int64_t)r;  // row past the descriptor base
       offB[i] = (uint32_t)(rb * p.ldb + c * 16);
-      kc |= (uint32_t)c << (4 * (CF::A_INSTR + i));
+      kc |= (uint32_t)c << (3 * (CF::A_INSTR + i));
     }
     lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
   }
@@ -680,7 +680,7 @@ struct DmaLoader {
     constexpr int NW = CF::NW;
     const uint32_t st = lds0 + (uint32_t)(stage * CF::STAGE_BYTES);
     const uint32_t kbyte = (uint32_t)kb * BK;
-    const int64_t kchunk = (int64_t)kbyte + (int64_t)(((kc >> (4 * n)) & 7u) * 16u);
+    const int64_t kchunk = (int64_t)kbyte + (int64_t)(((kc >> (3 * n)) & 7u) * 16u);
     if (n < CF::A_INSTR) {
       const uint32_t off = (KFULL || kchunk < K) ? offA[n] : kOob;
       dma_b128(rsA, st + (uint32_t)((wave + NW * n) * 1024), off, kbyte);
@@ -1102,6 +1102,12 @@ constexpr int kSkinnyCfg[2] = {DSFP8_SKINNY};
 constexpr int kSkinnyWaves = kSkinnyCfg[0];
 constexpr int kSkinnyDepth = kSkinnyCfg[1];
 constexpr int kSkinnyRows = 16;
+// 17 to 32 rows take the two-fragment form only while N is small (few
+// workgroups, each re-reading all rows of A from L2 per 16 columns).
+#ifndef DSFP8_SKINNY32_MAXN
+#define DSFP8_SKINNY32_MAXN 0
+#endif
+constexpr int64_t kSkinny32MaxN = DSFP8_SKINNY32_MAXN;
 
 // 32 bytes of one operand row for a lane: two 16-byte chunks; a chunk at or
 // past K (K is a multiple of 16 here) or of a row outside the matrix reads as
@@ -1116,66 +1122,86 @@ __device__ __forceinline__ v8i skinny_frag(const uint8_t* row, bool valid, int64
   return f;
 }
 
-template <bool POW2>
+// FRAGS 16-row activation fragments (up to 16 * FRAGS rows): each wave
+// multiplies its weight fragment by every activation fragment of a K-block.
+template <bool POW2, int FRAGS>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs p) {
-  __shared__ float red[kSkinnyWaves][64][4];
+  __shared__ float red[kSkinnyWaves][FRAGS][64][4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, fg = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t K = p.K;
   const int64_t nk = (K + BK - 1) / BK;
-  // Column layout (weight fragment first): lane (fr, fg) ends with outputs
-  // C[fr][n0 + 4fg + v]; it loads weight row n0 + fr and activation row fr,
-  // bytes 32fg .. 32fg + 31 of each K-block.
-  const bool bv = n0 + fr < p.N, av = fr < p.M;
+  // Column layout (weight fragment first): lane (fr, fg) of fragment f ends
+  // with outputs C[16f + fr][n0 + 4fg + v]; it loads weight row n0 + fr and
+  // activation rows 16f + fr, bytes 32fg .. 32fg + 31 of each K-block.
+  const bool bv = n0 + fr < p.N;
   const uint8_t* brow = p.B + (bv ? n0 + fr : 0) * p.ldb;
-  const uint8_t* arow = p.A + (av ? fr : 0) * p.lda;
-  const float* asr = p.a_s + (av ? fr : 0) * p.as_rs;
   const float* bsr = p.b_s + (n0 / BK) * p.ldbs;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool av[FRAGS];
+  const uint8_t* arow[FRAGS];
+  const float* asr[FRAGS];
+#pragma unroll
+  for (int f = 0; f < FRAGS; ++f) {
+    const int r = 16 * f + fr;
+    av[f] = r < p.M;
+    arow[f] = p.A + (av[f] ? r : 0) * p.lda;
+    asr[f] = p.a_s + (av[f] ? r : 0) * p.as_rs;
+  }
+  v4f acc[FRAGS];
+#pragma unroll
+  for (int f = 0; f < FRAGS; ++f) acc[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t kb0 = wave; kb0 < nk; kb0 += (int64_t)kSkinnyWaves * kSkinnyDepth) {
-    v8i bf[kSkinnyDepth], af[kSkinnyDepth];
-    float sa[kSkinnyDepth], sb[kSkinnyDepth];
+    v8i bf[kSkinnyDepth], af[kSkinnyDepth][FRAGS];
+    float sa[kSkinnyDepth][FRAGS], sb[kSkinnyDepth];
 #pragma unroll
     for (int d = 0; d < kSkinnyDepth; ++d) {
       const int64_t kb = kb0 + (int64_t)d * kSkinnyWaves;
       const bool live = kb < nk;
       const int64_t k = kb * BK + 32 * fg;
       bf[d] = skinny_frag(brow, bv && live, k, K);
-      af[d] = skinny_frag(arow, av && live, k, K);
-      sa[d] = live && av ? asr[kb * p.as_ks] : 0.0f;
+#pragma unroll
+      for (int f = 0; f < FRAGS; ++f) {
+        af[d][f] = skinny_frag(arow[f], av[f] && live, k, K);
+        sa[d][f] = live && av[f] ? asr[f][kb * p.as_ks] : 0.0f;
+      }
       sb[d] = live ? bsr[kb] : 0.0f;
     }
 #pragma unroll
     for (int d = 0; d < kSkinnyDepth; ++d) {
       if (kb0 + (int64_t)d * kSkinnyWaves >= nk) break;
-      if constexpr (POW2) {
-        // a row past M carries scale 0 here, which the MFMA reads as 2^-127
-        // times a zero fragment: still zero
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af[d], acc, 0, 0, 0,
-                                                               (int)(__float_as_uint(sb[d]) >> 23), 0,
-                                                               (int)(__float_as_uint(sa[d]) >> 23));
-      } else {
-        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af[d], z, 0, 0, 0, 0, 0, 0);
-        const float sc = sa[d] * sb[d];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(part[v], sc, acc[v]);
+      for (int f = 0; f < FRAGS; ++f) {
+        if constexpr (POW2) {
+          // a row past M carries scale 0 here, which the MFMA reads as 2^-127
+          // times a zero fragment: still zero
+          acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af[d][f], acc[f], 0, 0, 0,
+                                                                    (int)(__float_as_uint(sb[d]) >> 23), 0,
+                                                                    (int)(__float_as_uint(sa[d][f]) >> 23));
+        } else {
+          const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d], af[d][f], z, 0, 0, 0, 0, 0, 0);
+          const float sc = sa[d][f] * sb[d];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[f][v] = __builtin_fmaf(part[v], sc, acc[f][v]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) red[wave][lane][v] = acc[v];
+  for (int f = 0; f < FRAGS; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][f][lane][v] = acc[f][v];
   __syncthreads();
-  // Thread t < 256 finishes output (row t / 16, column t % 16).
+  // Thread t < 256 * FRAGS finishes output (row t / 16, column t % 16).
   const int t = threadIdx.x;
-  if (t >= kSkinnyRows * 16) return;
+  if (t >= kSkinnyRows * FRAGS * 16) return;
   const int r = t >> 4, c = t & 15;
-  const int l = (c >> 2) * 16 + r, v = c & 3;
+  const int f = r >> 4, l = (c >> 2) * 16 + (r & 15), v = c & 3;
   float sum = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSkinnyWaves; ++w) sum += red[w][l][v];
+  for (int w = 0; w < kSkinnyWaves; ++w) sum += red[w][f][l][v];
   if (r < p.M && n0 + c < p.N) p.C[(int64_t)r * p.ldc + n0 + c] = __builtin_bit_cast(uint16_t, (__bf16)sum);
 }
 
@@ -1481,16 +1507,21 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // 16-column workgroup re-reads twice the weight's bytes of activations
 // (32 x 36864 x 7168: 112 vs 65 us).
 bool skinny_ok(const GemmArgs& a) {
-  return a.M <= kSkinnyRows && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) &&
-         aligned(a.B, 16);
+  const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && a.N <= kSkinny32MaxN);
+  return rows && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (skinny_ok(a)) {
     const dim3 grid((unsigned)((a.N + 15) / 16)), blk(64 * kSkinnyWaves);
-    if (a.pow2) hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, blk, 0, stream, a);
-    else hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, blk, 0, stream, a);
+    if (a.M <= kSkinnyRows) {
+      if (a.pow2) hipLaunchKernelGGL((skinny_gemm_kernel<true, 1>), grid, blk, 0, stream, a);
+      else hipLaunchKernelGGL((skinny_gemm_kernel<false, 1>), grid, blk, 0, stream, a);
+    } else {
+      if (a.pow2) hipLaunchKernelGGL((skinny_gemm_kernel<true, 2>), grid, blk, 0, stream, a);
+      else hipLaunchKernelGGL((skinny_gemm_kernel<false, 2>), grid, blk, 0, stream, a);
+    }
     return hipGetLastError();
   }
   const int splits = gemm_k_splits(a.M, a.N, a.K);
