@@ -317,8 +317,9 @@ hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
   if (a.h) vec = vec && aligned(a.h, 16) && (a.ldh % 8 == 0);
   const int64_t waves_per_wg = kThreads / 64;
   const int64_t want = (units + waves_per_wg * kUnroll - 1) / (waves_per_wg * kUnroll);
-  // Workgroups per CU (measured): 16 for the plain kernel, 8 for the fused one.
-  const int64_t cap = (int64_t)device_cu_count() * (fused ? 8 : 16);
+  // Workgroups per CU (measured): 32 for the plain kernel (1.5-3% faster than
+  // 16 on the dense-input, routed-row and gathered shapes), 8 for the fused one.
+  const int64_t cap = (int64_t)device_cu_count() * (fused ? 8 : 32);
   const int64_t grid = want < cap ? want : cap;
   // The multiply-shift division needs every wave-unit index the loop forms
   // (up to kUnroll grid-widths past the end) below 2^31.
