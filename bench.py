@@ -406,45 +406,58 @@ def graph_time(fn, iters, reps=5):
 def bench_act_quant(dev, iters):
     """act_quant alone at the workloads' activation shapes: `iters` launches
     back to back from a captured graph (the kernel's steady-state rate; the
-    per-launch event pair inside the step adds a few microseconds)."""
+    per-launch event pair inside the step adds a few microseconds), rotating
+    input/output sets of more than 512 MB in all (at most 64 sets) so the
+    256 MB Infinity Cache cannot serve the large shapes' repeats."""
     lib = ds._lib.load()
     res = {}
     for name, (M, K, fmt) in {"dense_ffn_input [4096,7168]": (4096, 7168, "fp32"),
                               "routed_rows [32768,7168]": (32768, 7168, "fp32"),
                               "decode [32,7168]": (32, 7168, "fp32"),
                               "ragged_ue8m0 [333,1000]": (333, 1000, "ue8m0")}.items():
-        x = I.device_normal((M, K), seed=801, std=1.0, device=dev, dtype=torch.bfloat16)
-        y = torch.empty((M, K), dtype=torch.uint8, device=dev)
-        s = ds.new_scales(M, kb(K), dev)
+        by = aq_bytes(M, K)
+        nsets = int(min(64, max(1, np.ceil(600e6 / by))))
+        sets = []
+        for i in range(nsets):
+            x = I.device_normal((M, K), seed=801 + i, std=1.0, device=dev, dtype=torch.bfloat16)
+            sets.append((x, torch.empty((M, K), dtype=torch.uint8, device=dev), ds.new_scales(M, kb(K), dev)))
         code = 1 if fmt == "ue8m0" else 0
 
-        def call(i, stream, x=x, y=y, s=s, M=M, K=K, code=code):
+        def call(i, stream, sets=sets, M=M, K=K, code=code):
+            x, y, s = sets[i % len(sets)]
             st = lib.dsfp8_act_quant(x.data_ptr(), M, K, K, y.data_ptr(), K, s.data_ptr(), s.stride(0), s.stride(1),
                                      code, stream)
             assert st == 0, st
 
-        us = graph_time(call, iters)
-        by = aq_bytes(M, K)
+        us = graph_time(call, max(iters, 2 * nsets))
         res[name] = {"us": round(us, 2), "gbs": round(by / us / 1e3, 1),
-                     "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
+                     "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3), "buffer_sets_rotated": nsets}
+        del sets
     return res
 
 
 def bench_dequant(dev, iters):
+    """weight_dequant of one [18432, 7168] weight per call, back to back from
+    a captured graph, rotating four weight/output sets (1.6 GB) so the 256 MB
+    Infinity Cache cannot serve repeats."""
     N, K = 18432, 7168
-    w = I.device_normal((N, K), seed=501, std=0.02, device=dev)
-    res = {"workload": "weight_dequant e4m3 [18432, 7168] -> bf16"}
+    res = {"workload": "weight_dequant e4m3 [18432, 7168] -> bf16", "buffer_sets_rotated": 4}
     for fmt in ("fp32", "ue8m0"):
-        q, S = ds.weight_quant(w, fmt)
-        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-        T = Timer()
-        for _ in range(3):
-            ds.weight_dequant(q, S, out=out)
-        torch.cuda.synchronize()
-        for _ in range(iters):
-            T.run("dq", lambda: ds.weight_dequant(q, S, out=out))
-        T.collect()
-        us = T.avg_us("dq")
+        sets = []
+        for i in range(4):
+            w = I.device_normal((N, K), seed=501 + i, std=0.02, device=dev)
+            q, S = ds.weight_quant(w, fmt)
+            del w
+            sets.append((q, S, torch.empty((N, K), dtype=torch.bfloat16, device=dev)))
+        lib = ds._lib.load()
+
+        def call(i, stream, sets=sets):
+            q, S, out = sets[i % len(sets)]
+            st = lib.dsfp8_weight_dequant(q.data_ptr(), N, K, K, S.data_ptr(), S.stride(0), out.data_ptr(), K, stream)
+            assert st == 0, st
+
+        us = graph_time(call, max(iters, 8))
+        del sets
         by = N * K * 3 + 4 * kb(N) * kb(K)
         res[fmt] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                     "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
