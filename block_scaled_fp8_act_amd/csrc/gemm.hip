@@ -1102,12 +1102,13 @@ constexpr int kSkinnyCfg[2] = {DSFP8_SKINNY};
 constexpr int kSkinnyWaves = kSkinnyCfg[0];
 constexpr int kSkinnyDepth = kSkinnyCfg[1];
 constexpr int kSkinnyRows = 16;
-// 17 to 32 rows take the two-fragment form only while N is small (few
-// workgroups, each re-reading all rows of A from L2 per 16 columns).
-#ifndef DSFP8_SKINNY32_MAXN
-#define DSFP8_SKINNY32_MAXN 0
-#endif
-constexpr int64_t kSkinny32MaxN = DSFP8_SKINNY32_MAXN;
+// 17 to 32 rows take the two-fragment form for 2048 < N <= 8192 only
+// (measured against split K: 32x7168x2048 10.9 vs 13.7 us, 32x4096x7168 14.0
+// vs 14.6 us; with N <= 2048 there are too few workgroups to stream the
+// weight (32x1536x7168: 13.4 vs 12.5 us), and beyond 8192 every 16-column
+// workgroup's re-read of all rows of A outweighs the saving (32x18432x7168:
+// 60 vs 55 us)).
+constexpr int64_t kSkinny32MinN = 2048, kSkinny32MaxN = 8192;
 
 // 32 bytes of one operand row for a lane: two 16-byte chunks; a chunk at or
 // past K (K is a multiple of 16 here) or of a row outside the matrix reads as
@@ -1507,7 +1508,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // 16-column workgroup re-reads twice the weight's bytes of activations
 // (32 x 36864 x 7168: 112 vs 65 us).
 bool skinny_ok(const GemmArgs& a) {
-  const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && a.N <= kSkinny32MaxN);
+  const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && a.N > kSkinny32MinN && a.N <= kSkinny32MaxN);
   return rows && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16);
 }
 

@@ -193,10 +193,12 @@ def _sampled_product(M, N, K, seed, row_pick, nblocks, fmt="fp32"):
 
 
 @pytest.mark.parametrize("M,N,K,fmt", [(1, 4608, 7168, "fp32"), (16, 7168, 2048, "fp32"), (8, 1536, 7168, "ue8m0"),
-                                       (5, 300, 1040, "fp32"), (16, 129, 16, "ue8m0")])
+                                       (5, 300, 1040, "fp32"), (16, 129, 16, "ue8m0"),
+                                       (32, 7168, 2048, "fp32"), (17, 2100, 1040, "ue8m0"), (24, 4100, 528, "fp32")])
 def test_decode_rows(M, N, K, fmt):
-    # at most 16 rows with K % 16 == 0: the kernel that splits K across the
-    # waves of one workgroup per 16 columns (ragged N and K included)
+    # at most 16 rows with K % 16 == 0 (and 17 to 32 rows for 2048 < N <= 8192,
+    # two activation fragments): the kernel that splits K across the waves of
+    # one workgroup per 16 columns (ragged N and K included)
     a, a_s, b, b_s = operands(M, N, K, I.DECODE_QA, ue8m0=(fmt == "ue8m0"), outliers=0.01)
     for layout in ("kb", "row"):
         check_gemm_full(run(a, a_s, b, b_s, layout, scale_fmt=fmt), a, a_s, b, b_s, f"{M}x{N}x{K} {fmt} {layout}")
