@@ -17,6 +17,14 @@
 // Workgroups are mapped to tiles so that each XCD (workgroup i runs on XCD
 // i % 8) owns a contiguous range of tiles, ordered in groups of GROUP_M tile
 // rows, which keeps the A and B panels in use on one XCD inside its L2.
+//
+// Kernels: gemm_persistent_kernel (one workgroup per CU walking its XCD's
+// 256x256 tiles) for large dense products, plain or with the SiLU gate and
+// act_quant in the epilogue; gemm_kernel (one workgroup per tile, split K
+// through a workspace when there are few tiles) otherwise;
+// skinny_gemm_kernel for decode rows; grouped_merged_kernel for the
+// per-expert products (three tile heights in one launch, scheduled by
+// tile_schedule_kernel from the device-side offsets).
 #include "device.h"
 #include "launch.h"
 
