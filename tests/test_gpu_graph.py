@@ -103,6 +103,38 @@ def test_dense_step_graph(fmt):
     assert fro <= 2e-2, f"relative Frobenius error {fro:.3e}"
 
 
+def test_dense_step_graph_persistent_products():
+    """A dense step large enough that both products run the persistent kernel
+    (6 x 43 = 258 tiles of 256 x 256 each, M, N and K tails): the replays
+    equal the eager step byte for byte (the products' parity against the
+    oracle at these paths is checked in the product tests)."""
+    M, D, Fi = 1300, 11008, 5504
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = (torch.randn((M, D), device="cuda", generator=g)).to(torch.bfloat16)
+    q13, s13 = ds.weight_quant(torch.randn((2 * Fi, D), device="cuda", generator=g) * 0.02)
+    q2, s2 = ds.weight_quant(torch.randn((D, Fi), device="cuda", generator=g) * 0.02)
+    xq = torch.empty((M, D), dtype=torch.uint8, device="cuda")
+    xsc = ds.new_scales(M, ds.kblocks(D), "cuda")
+    hq = torch.empty((M, Fi), dtype=torch.uint8, device="cuda")
+    hsc = ds.new_scales(M, ds.kblocks(Fi), "cuda")
+    out = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        ds.act_quant(x, out=(xq, xsc))
+        ds.gemm_silu_mul_act_quant(xq, xsc, q13, s13, out=(hq, hsc))
+        ds.gemm(hq, hsc, q2, s2, out=out)
+
+    step()
+    gr = _capture(step)
+    seeds = [11, 12, 13, 14]
+
+    def refill(r):
+        gg = torch.Generator(device="cuda").manual_seed(seeds[r])
+        x.copy_(torch.randn((M, D), device="cuda", generator=gg).to(torch.bfloat16))
+
+    _replay_matches_eager(gr, step, [xq, xsc, hq, hsc, out], refill)
+
+
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
 def test_routed_step_graph(fmt):
     T, D, Fi, E, k = 160, 512, 256, 8, 2
