@@ -1263,44 +1263,56 @@ __device__ __forceinline__ void class_rows(int64_t n, int c, int classes, const 
 }
 
 // tile_start[c * (E + 1) + e] = number of class-c row tiles of the experts
-// before e.  One workgroup.
+// before e.  One workgroup of 16 waves takes 1024 experts per step and all
+// classes at once: an inclusive scan inside each wave (lane shuffles), the
+// 16 wave totals through LDS, and a running carry per class across steps.
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmArgs p) {
+  constexpr int kWaves = 1024 / 64;
   const int32_t* offsets = p.offsets;
   const int64_t E = p.E, M = p.M;
+  const int C = p.grp_classes;
   int32_t* tile_start = p.tile_start;
-  __shared__ int32_t part[1024];
-  __shared__ int32_t carry;
-  const int t = threadIdx.x;
-  for (int c = 0; c < p.grp_classes; ++c) {
-    int32_t* ts = tile_start + (int64_t)c * (E + 1);
-    if (t == 0) {
-      carry = 0;
-      ts[0] = 0;
+  __shared__ int32_t wsum[kMaxClasses][kWaves];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int32_t carry[kMaxClasses] = {0, 0, 0};
+  if (t < C) tile_start[(int64_t)t * (E + 1)] = 0;
+  for (int64_t base = 0; base < E; base += 1024) {
+    const int64_t e = base + t;
+    int32_t v[kMaxClasses] = {0, 0, 0};
+    if (e < E) {
+      int64_t lo, hi;
+      expert_rows(offsets, e, M, lo, hi);
+#pragma unroll
+      for (int c = 0; c < kMaxClasses; ++c) {
+        if (c < C) {
+          int64_t a, b;
+          class_rows(hi - lo, c, C, p.grp_h, a, b);
+          v[c] = (int32_t)((b - a + p.grp_h[c] - 1) / p.grp_h[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(v[c], d, 64);
+        if (lane >= d) v[c] += y;
+      }
+      if (lane == 63) wsum[c][w] = v[c];
     }
     __syncthreads();
-    for (int64_t base = 0; base < E; base += 1024) {
-      const int64_t e = base + t;
-      int32_t cnt = 0;
-      if (e < E) {
-        int64_t lo, hi;
-        expert_rows(offsets, e, M, lo, hi);
-        int64_t a, b;
-        class_rows(hi - lo, c, p.grp_classes, p.grp_h, a, b);
-        cnt = (int32_t)((b - a + p.grp_h[c] - 1) / p.grp_h[c]);
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+      int32_t before = carry[c];
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const int32_t s = wsum[c][i];
+        before += i < w ? s : 0;
+        carry[c] += s;
       }
-      part[t] = cnt;
-      __syncthreads();
-      for (int d = 1; d < 1024; d <<= 1) {
-        const int32_t add = t >= d ? part[t - d] : 0;
-        __syncthreads();
-        part[t] += add;
-        __syncthreads();
-      }
-      if (e < E) ts[e + 1] = carry + part[t];
-      __syncthreads();
-      if (t == 1023) carry += part[1023];
-      __syncthreads();
+      if (c < C && e < E) tile_start[(int64_t)c * (E + 1) + e + 1] = before + v[c];
     }
+    __syncthreads();  // wsum is rewritten by the next step
   }
 }
 

@@ -82,6 +82,17 @@ def test_grouped_ue8m0(counts, N, K):
     _check_all(C, a, a_s, b, b_s, off, f"ue8m0 {counts}")
 
 
+def test_many_experts():
+    """More experts than the tile schedule takes in one step (1024): the
+    per-class tile counts carry across steps; tiles of all three heights."""
+    g = np.random.default_rng(17)
+    counts = g.choice([0, 1, 2, 3, 5], size=1500)
+    counts[[3, 700, 1030, 1499]] = [70, 130, 300, 257]
+    a, a_s, b, b_s, off = _case(counts, 128, 256, 21)
+    C = _run(a, a_s, b, b_s, off)
+    _check_all(C, a, a_s, b, b_s, off, "1500 experts")
+
+
 def test_single_expert_equals_dense():
     # 9 x 16 output tiles: enough that the dense product does not split K, so
     # both run the same tile code in the same accumulation order.
