@@ -347,8 +347,9 @@ dsfp8_status grouped_glu(const void* A, int64_t a_rows, int64_t lda, const float
   if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
   if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
   if (rows != nullptr) {
-    // one buffer descriptor spans every row of A (32-bit offsets)
-    if (a_rows * lda + K >= ((int64_t)1 << 31)) return DSFP8_ERR_UNSUPPORTED;
+    // one buffer descriptor spans every row of A (32-bit offsets); lda is
+    // tested first so that the product cannot overflow
+    if (lda >= ((int64_t)1 << 31) || a_rows * lda + K >= ((int64_t)1 << 31)) return DSFP8_ERR_UNSUPPORTED;
     a.a_rows = rows;
     a.a_rows_n = a_rows;
   }

@@ -284,6 +284,8 @@ def test_grouped_gated_gather_validation(lib):
     assert call(F=200, ldy=200) == UNSUP
     # one descriptor spans all of A: a_rows * lda + K must stay below 2^31
     assert call(a_rows=(1 << 31) // 256, as_ks=(1 << 31) // 256, lda=256) == UNSUP
+    # ... also where a_rows * lda would overflow 64 bits
+    assert call(a_rows=1 << 25, as_ks=1 << 25, lda=1 << 39) == UNSUP
     # no rows: nothing to do, nothing launched (the pointers are never touched)
     assert call(M=0) == OK
     assert call(M=0, rows=None) == OK
