@@ -618,6 +618,10 @@ def only(kernel, reps, dev):
                                                                 out=(b["hq"], b["hs"])),
             "gemm_down": lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"]),
         }
+        if kernel == "weight_dequant":
+            # w1 of the dense FFN, [18432, 7168] (the first F rows of the stacked [w1; w3])
+            dq = torch.empty((F, b["q13"].shape[1]), dtype=torch.bfloat16, device=dev)
+            fns[kernel] = lambda: ds.weight_dequant(b["q13"][:F], b["s13"][:F // 128], out=dq)
         dense_step(st, T)  # produce valid inputs for every stage
         torch.cuda.synchronize()
         for _ in range(reps):
@@ -633,7 +637,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["act_quant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
+    ap.add_argument("--only", choices=["act_quant", "weight_dequant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
                                        "copy", "routed_experts"],
                     help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
                          "(for rocprofv3)")
