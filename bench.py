@@ -531,7 +531,10 @@ def cpu_baseline(budget_s=15.0):
     timing; each timed chunk runs act_quant, the up product, the gate,
     act_quant of h and the down product, all in the oracle.  Chunks run until
     ``budget_s`` seconds of oracle time have passed.  Reported as the sample's
-    GEMM flop per second.
+    GEMM flop per second.  ``cores`` is the number of threads the oracle
+    actually used (the BLAS pool that runs its fp64 products; its quantisers
+    are single-threaded NumPy); ``affinity_cpus`` is the number of host CPUs
+    the process may run on.
     """
     import threadpoolctl
     from oracle import gemm as G
@@ -561,6 +564,7 @@ def cpu_baseline(budget_s=15.0):
     except Exception:
         threads = 1
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "blas_threads": int(threads), "affinity_cpus": len(os.sched_getaffinity(0)),
             "kind": "oracle", "seconds": round(dt, 2), "chunks": done,
             "sample": f"dense FFN step on {done} chunks of 128 tokens x (3072 up-projection outputs, K=7168) "
                       "+ SiLU gate + (1536 down outputs, K=1536); fp64 products through NumPy BLAS, "
@@ -593,8 +597,9 @@ def recorded_traffic():
 
 # ---- main --------------------------------------------------------------------------------------
 
-def only(kernel, reps, dev):
-    """Run one kernel of the dense step `reps` times (for counter collection)."""
+def only(kernel, reps, dev, fmt="fp32"):
+    """Run one kernel of the dense step `reps` times (for counter collection),
+    with fp32 or ue8m0 scales throughout."""
     if kernel == "routed_experts":
         print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps)}))
         return
@@ -606,17 +611,17 @@ def only(kernel, reps, dev):
         for _ in range(reps):
             dst.copy_(src)
     else:
-        st = setup_dense(dev, unfused=kernel in ("gemm_up", "silu_mul_act_quant"))
+        st = setup_dense(dev, fmt, unfused=kernel in ("gemm_up", "silu_mul_act_quant"))
         T = Timer()
         b, F = st["b"], st["F"]
         fns = {
-            "act_quant": lambda: ds.act_quant(b["x"], out=(b["xq"], b["xs"])),
-            "gemm_up_gate": lambda: ds.gemm_silu_mul_act_quant(b["xq"], b["xs"], b["q13"], b["s13"],
+            "act_quant": lambda: ds.act_quant(b["x"], fmt, out=(b["xq"], b["xs"])),
+            "gemm_up_gate": lambda: ds.gemm_silu_mul_act_quant(b["xq"], b["xs"], b["q13"], b["s13"], fmt,
                                                                out=(b["hq"], b["hs"])),
-            "gemm_up": lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"]),
-            "silu_mul_act_quant": lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:],
+            "gemm_up": lambda: ds.gemm(b["xq"], b["xs"], b["q13"], b["s13"], out=b["h13"], scale_fmt=fmt),
+            "silu_mul_act_quant": lambda: ds.silu_mul_act_quant(b["h13"][:, :F], b["h13"][:, F:], fmt,
                                                                 out=(b["hq"], b["hs"])),
-            "gemm_down": lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"]),
+            "gemm_down": lambda: ds.gemm(b["hq"], b["hs"], b["q2"], b["s2"], out=b["out"], scale_fmt=fmt),
         }
         if kernel == "weight_dequant":
             # w1 of the dense FFN, [18432, 7168] (the first F rows of the stacked [w1; w3])
@@ -642,6 +647,7 @@ def main():
                     help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
                          "(for rocprofv3)")
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--fmt", choices=["fp32", "ue8m0"], default="fp32", help="scale format for --only")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -654,7 +660,7 @@ def main():
     ds._lib.load()
     dev = torch.device("cuda:0")
     if args.only:
-        only(args.only, args.reps, dev)
+        only(args.only, args.reps, dev, args.fmt)
         return
     props = torch.cuda.get_device_properties(dev)
 

@@ -75,11 +75,16 @@ __device__ __forceinline__ float block_scale(float amax, bool ue8m0) {
 }
 
 // x / s, correctly rounded, given r = RN(1/s): q = RN(x*r), then one
-// correction with the exact remainder t = q*s - x (formed by an fma).  The
-// result equals the IEEE quotient for every pair (x, s) that act_quant can
-// produce; this is checked exhaustively over all bf16 significands of x and
-// all scale significands on the CPU.  The sign of a zero quotient is kept:
-// for x = -0, q = -0 and t = +0, so fma(-t, r, q) = -0.
+// correction with the exact remainder t = q*s - x (formed by an fma), i.e.
+// Markstein's final correction step for division (P. Markstein, "Computation
+// of elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990).  The result equals the IEEE quotient for every pair
+// (x, s) that act_quant can produce (bf16 x; s from a bf16 block maximum);
+// this is checked by an exact rational computation over all bf16
+// significands of x and all scale significands on the CPU.  Callers outside
+// that domain (fp32 inputs) use the IEEE division instead.  The sign of a
+// zero quotient is kept: for x = -0, q = -0 and t = +0, so
+// fma(-t, r, q) = -0.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   float q = x * r;
   float t = __builtin_fmaf(q, s, -x);

@@ -38,10 +38,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;
 constexpr int kXcds = 8;
-#ifndef DSFP8_GROUP_M
-#define DSFP8_GROUP_M 8
-#endif
-constexpr int kGroupM = DSFP8_GROUP_M;
+constexpr int kGroupM = 8;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct Cfg {
@@ -197,11 +194,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& t, 
     if (row >= row_lim || col >= N) continue;
     uint16_t* dst = p.C + row * p.ldc + col;
     if (cvec && col + 8 <= N) {
-#ifdef DSFP8_NT_STORE
-      __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst));
-#else
       *reinterpret_cast<u32x4*>(dst) = v[it];
-#endif
     } else {
       const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
       for (int e = 0; e < 8 && col + e < N; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
@@ -443,13 +436,21 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // The loads are issued from inline assembly so that the compiler, which
 // cannot tell the stages of the ring apart, does not add a vmcnt(0) wait in
 // front of every LDS read; the kernel waits for each stage itself.  M0 holds
-// the wave's LDS destination and is set in the same statement; the s_nop
-// provides the wait state required between an SALU write of M0 and an LDS
-// DMA that reads it.  Nothing else in these kernels uses M0 (no LDS DMA by
-// the compiler, no indexed register access), so the value need not survive.
+// the wave's LDS destination and is set in the same statement (and declared
+// clobbered, so the compiler keeps nothing of its own in M0 across it); the
+// s_nop provides the wait state required between an SALU write of M0 and an
+// LDS DMA that reads it.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
+
+// M0 is a reserved register, so clang warns that a clobber of it is not
+// saved and restored around the statement; that is intended (nothing needs
+// the old value), and the clobber still records the write of M0 in the
+// statement's dependencies, so no instruction of the compiler's that reads
+// M0 is moved across it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 
 // Byte address of lane l: rsrc base + voff + soff (the scalar part carries the
 // K-block offset, so the per-lane offsets stay fixed over the K loop).
@@ -457,7 +458,7 @@ __device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, uint32_t voff
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // The same with the nontemporal hint: for weight panels that one tile
@@ -466,7 +467,7 @@ __device__ __forceinline__ void dma_b128_nt(i32x4 rsrc, uint32_t lds, uint32_t v
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                :
                : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Per-lane 64-bit addresses: each active lane fetches one dword from anywhere.
@@ -474,8 +475,10 @@ __device__ __forceinline__ void dma_gather_b32(uint32_t lds, const float* addr) 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dword %1, off"
                :
                : "s"(lds), "v"(addr)
-               : "memory");
+               : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // The lane index behind an empty statement: values derived from it are
 // computed where they are used instead of being hoisted out of a persistent
@@ -528,20 +531,11 @@ struct DmaCfg {
 // products with too few of those tiles and split-K products: 128x128 tiles,
 // 4 waves of 64x64 (two workgroups per CU).
 // Large dense products run as one persistent workgroup per CU.
-#ifndef DSFP8_PERSISTENT
-#define DSFP8_PERSISTENT 1
-#endif
-#ifndef DSFP8_DMA_TILE
-#define DSFP8_DMA_TILE 256, 256, 2, 4, 2
-#endif
-using CfgDmaBig = DmaCfg<DSFP8_DMA_TILE>;
+using CfgDmaBig = DmaCfg<256, 256, 2, 4, 2>;
 using CfgDma = DmaCfg<128, 128, 2, 2, 2>;
 // Dense products of 17 to 64 rows (and their split-K form): 64-row tiles,
 // 4 waves of 64x32.
-#ifndef DSFP8_GROUPED_TILE
-#define DSFP8_GROUPED_TILE 64, 128, 1, 4, 2
-#endif
-using CfgGrp = DmaCfg<DSFP8_GROUPED_TILE>;
+using CfgGrp = DmaCfg<64, 128, 1, 4, 2>;
 // Gated form, and the grouped classes of at most 64 and 65-128 rows of both
 // forms: 256-column tiles (for the gated form 128 columns of each half),
 // 8 waves of 32x64 or 64x64; the large dense tile otherwise.  The small tiles
@@ -550,14 +544,8 @@ using CfgGrp = DmaCfg<DSFP8_GROUPED_TILE>;
 // measured 8% faster on the routed-expert up-projection, whose small experts
 // stream their weights once.  With all three classes at 8 waves, a grouped
 // product runs them in one launch (grouped_merged_kernel).
-#ifndef DSFP8_GLU64_TILE
-#define DSFP8_GLU64_TILE 64, 256, 2, 4, 3
-#endif
-#ifndef DSFP8_GLU128_TILE
-#define DSFP8_GLU128_TILE 128, 256, 2, 4, 3
-#endif
-using CfgGlu64 = DmaCfg<DSFP8_GLU64_TILE>;
-using CfgGlu128 = DmaCfg<DSFP8_GLU128_TILE>;
+using CfgGlu64 = DmaCfg<64, 256, 2, 4, 3>;
+using CfgGlu128 = DmaCfg<128, 256, 2, 4, 3>;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -903,12 +891,9 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, const TileRef& 
 // Workgroup i runs on XCD i % 8.  Renumber ids 0..total-1 so that each XCD
 // owns one contiguous range (and so shares its L2 among neighbouring tiles).
 __device__ __forceinline__ int64_t xcd_contiguous(int64_t pid, int64_t total) {
-#ifndef DSFP8_NO_XCD_REMAP
   const int64_t q = total / kXcds, r = total % kXcds;
   const int64_t xcd = pid % kXcds, idx = pid / kXcds;
-  pid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-#endif
-  return pid;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
 // Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges, then
@@ -1103,12 +1088,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 // the per-wave sums are then added in wave order through LDS and rounded to
 // bf16.  No split of K across workgroups, so no fp32 partials and no second
 // kernel.
-#ifndef DSFP8_SKINNY
-#define DSFP8_SKINNY 16, 3
-#endif
-constexpr int kSkinnyCfg[2] = {DSFP8_SKINNY};
-constexpr int kSkinnyWaves = kSkinnyCfg[0];
-constexpr int kSkinnyDepth = kSkinnyCfg[1];
+constexpr int kSkinnyWaves = 16;
+constexpr int kSkinnyDepth = 3;
 constexpr int kSkinnyRows = 16;
 // 17 to 32 rows take the two-fragment form for 2048 < N <= 8192 only
 // (measured against split K: 32x7168x2048 10.9 vs 13.7 us, 32x4096x7168 14.0
@@ -1571,11 +1552,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) <= 0) {
-#if DSFP8_PERSISTENT
     DSFP8_LAUNCH_DMA(gemm_persistent_kernel, CfgDmaBig, false, dim3((unsigned)device_cu_count()), stream, a);
-#else
-    DSFP8_LAUNCH_DMA(gemm_kernel, CfgDmaBig, false, dense_grid<CfgDmaBig>(a), stream, a);
-#endif
     return hipGetLastError();
   }
   if (a.M <= CfgGrp::BM && pick_vec<CfgGrp>(a) <= 0) {
@@ -1668,11 +1645,7 @@ hipError_t launch_gemm_glu(const GemmArgs& a, hipStream_t stream) {
   auto grid = [&](int bm) { return dim3((unsigned)(((a.M + bm - 1) / bm) * nt)); };
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * nt;
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count())
-#if DSFP8_PERSISTENT
     DSFP8_LAUNCH_DMA(gemm_persistent_kernel, CfgDmaBig, true, dim3((unsigned)device_cu_count()), stream, a);
-#else
-    DSFP8_LAUNCH_DMA(gemm_kernel, CfgDmaBig, true, grid(CfgDmaBig::BM), stream, a);
-#endif
   else if (a.M > CfgGlu64::BM)
     DSFP8_LAUNCH_DMA(gemm_kernel, CfgGlu128, true, grid(CfgGlu128::BM), stream, a);
   else
@@ -1691,3 +1664,4 @@ size_t grouped_workspace_bytes(int64_t E) {
 }
 
 }  // namespace dsfp8
+

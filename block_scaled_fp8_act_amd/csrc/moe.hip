@@ -24,9 +24,14 @@
 // Combine: one token per workgroup row, 8 columns per lane; the token's
 // contributions are taken in increasing expert order, each weighted product
 // rounded to bf16 and each addition rounded to bf16, as the pages' bf16 loop
-// computes them.  A product of two bf16 values and the sum of two bf16 values
-// are exact in fp32, so one fp32 operation followed by bf16 rounding gives
-// the correctly rounded bf16 result.
+// computes them.  Each step is one fp32 operation followed by rounding to
+// bf16, and that equals the correctly rounded bf16 result: a product of two
+// bf16 values (8-bit significands) is exact in fp32; a sum of two bf16 values
+// is not always exact in fp32 (exponents more than 16 apart), but rounding it
+// first to fp32 and then to bf16 gives the same bf16 value as rounding the
+// exact sum once, because fp32's 24-bit significand is at least 2 * 8 + 2
+// bits (double rounding to nearest is then innocuous; S. A. Figueroa, "When
+// is double rounding innocuous?", 1995).
 #include "device.h"
 #include "launch.h"
 

@@ -3,8 +3,10 @@
  *
  * C ABI of libdsfp8.so.  Every entry point takes plain device pointers and
  * sizes, enqueues its kernels on the caller's HIP stream and returns without
- * synchronising.  The library allocates no memory and keeps no mutable global
- * state; all buffers are owned by the caller.
+ * synchronising.  The library allocates no memory; all buffers are owned by
+ * the caller.  Its only global state is a per-device cache of the
+ * compute-unit count (read once with hipDeviceGetAttribute, used to size
+ * grids).
  *
  * Sources of the operations (the DeepSeek-V3 inference code as described by):
  *   [AG]  "DeepSeek-V3 Administrator & Developer Guide" (doccompiler.ai)

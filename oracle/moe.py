@@ -23,9 +23,13 @@ Readings taken where the pages are silent:
   dtype, section 1.3).  Each contribution ``expert_out * w`` is the product of
   two bf16 tensors, rounded once to bf16; each ``y += p`` is a bf16 addition,
   rounded once; the additions for a token happen in increasing expert order
-  (the loop order).  Both operations are formed exactly in fp64 here (a
-  product of two 8-bit significands, or a sum of two bf16 values, is exact in
-  fp64) and rounded once to bf16, nearest-even.
+  (the loop order).  Both operations are formed in fp64 here and rounded to
+  bf16, nearest-even, which equals rounding the exact result once: a product
+  of two 8-bit significands is exact in fp64; a sum of two bf16 values is
+  exact in fp64 unless their exponents are more than 45 apart, and even then
+  the fp64 rounding cannot change the bf16 result, because 53 bits are at
+  least 2 * 8 + 2 (double rounding to nearest is innocuous at that precision;
+  S. A. Figueroa, "When is double rounding innocuous?", 1995).
 * A token lists each expert at most once (top-k of distinct experts).
 """
 

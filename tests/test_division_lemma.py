@@ -12,6 +12,16 @@ is invariant under scaling x and s by powers of two while every intermediate
 stays normal, which holds whenever the quotient is large enough (>= 2^-11) to
 round to a non-zero e4m3 code; smaller quotients encode to a signed zero
 either way.  For ue8m0 scales (powers of two) every step is exact.
+
+The correction step is Markstein's (P. Markstein, IBM J. Res. Dev. 34(1),
+1990); his theorem gives correct rounding under conditions on the
+reciprocal and the first quotient, and this exhaustive rational check is
+what establishes it on the domain above.  That domain is every use of the
+scheme in the library: act_quant, act_quant of gathered rows and the SiLU
+gate's quantisation (standalone and in the gated product's epilogue) all
+divide a bf16 value by a scale derived from a bf16 block maximum.  The
+weight quantiser, whose fp32 weights lie outside it, uses the correctly
+rounded IEEE division instead.
 """
 
 from fractions import Fraction

@@ -183,10 +183,12 @@ def test_silu_mul_act_quant(M, I_, fmt):
     colblk = np.arange(I_) // 128
     mask = clean[:, colblk]
     assert np.array_equal(yg[mask], yr[mask])
-    # and (y, s) are exactly act_quant of the h this call produced (GPU vs GPU)
-    y2, s2 = ds.act_quant(h, fmt)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
+    # and on every block, (y, s) are exactly the oracle's act_quant of the h
+    # this call produced (the stage-by-stage check: the quantiser is judged
+    # on the gate's own output)
+    yo, so = Q.act_quant(hg, ue8m0=(fmt == "ue8m0"))
+    assert np.array_equal(host_f32_bits(s), so.view(np.uint32)), "scales differ from act_quant(h)"
+    assert np.array_equal(yg, yo), "codes differ from act_quant(h)"
 
 
 def test_silu_mul_strided_halves():

@@ -101,8 +101,18 @@ def oracle_gate(a, a_s, w, w_s):
     return C, hb, absC, h
 
 
+def check_quant_of_h(y, s, h, ue8m0, what):
+    """The quantisation stage on its own input: on every block, (y, s) must be
+    bit for bit the oracle's act_quant of the h that the kernel computed."""
+    yo, so = Q.act_quant(h, ue8m0=ue8m0)
+    assert np.array_equal(host_f32_bits_np(s), so.view(np.uint32)), f"{what}: scales differ from act_quant(h)"
+    assert np.array_equal(np.asarray(y), yo), f"{what}: codes differ from act_quant(h)"
+
+
 def check_against_oracle(y, s, h, a, a_s, w, w_s, ue8m0, what):
-    """Element-wise bound of the module docstring, rows of one expert."""
+    """Element-wise bound of the module docstring, rows of one expert, and the
+    quantisation stage bit-exact on the kernel's own h."""
+    check_quant_of_h(y, s, h, ue8m0, what)
     F_ = w.shape[0] // 2
     C, hb, absC, h_ref_bits = oracle_gate(a, a_s, w, w_s)
     h1 = F.bf16_to_f32(hb[:, :F_]).astype(np.float64)
@@ -178,6 +188,7 @@ def test_integer_operands_exact(M, F_, K, fmt):
     assert np.array_equal(host_f32_bits_np(s)[clean], sr.view(np.uint32)[clean])
     mask = clean[:, np.arange(F_) // 128]
     assert np.array_equal(y[mask], yr[mask])
+    check_quant_of_h(y, s, h, fmt == "ue8m0", f"{M}x{F_}x{K} {fmt}")
 
 
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
@@ -317,6 +328,7 @@ def test_grouped_integer_operands_exact():
         assert np.array_equal(host_f32_bits_np(s[lo:hi])[clean], sr.view(np.uint32)[clean])
         mask = clean[:, np.zeros(F_, int)]
         assert np.array_equal(y[lo:hi][mask], yr[mask])
+        check_quant_of_h(y[lo:hi], s[lo:hi], h[lo:hi], False, f"expert {e}")
 
 
 def test_routed_expert_size_sampled():
