@@ -25,6 +25,8 @@ SIGNATURES = {
     "dsfp8_grouped_gemm": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p,
                                 _i64, _i, _p, _sz, _p]),
     "dsfp8_grouped_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "dsfp8_grouped_gemm_noalloc": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64,
+                                        _p, _i64, _i, _p]),
     "dsfp8_gemm_silu_mul_act_quant": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64,
                                            _p, _i64, _i64, _p, _i64, _i, _p]),
     "dsfp8_grouped_gemm_silu_mul_act_quant": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64,

@@ -94,6 +94,7 @@ const char* dsfp8_status_string(dsfp8_status st) {
     case DSFP8_ERR_LAUNCH: return "the HIP runtime reported a launch failure";
     case DSFP8_ERR_DTYPE: return "unknown element type";
     case DSFP8_ERR_UNSUPPORTED: return "the fused form does not support this operand layout";
+    case DSFP8_ERR_SCRATCH: return "the problem needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -240,11 +241,13 @@ size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N,
   return dsfp8::grouped_workspace_bytes(E);
 }
 
-dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
-                                int64_t as_kb_stride, const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
-                                const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* C,
-                                int64_t ldc, int scale_fmt, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+namespace {
+
+// Arguments of the grouped product (everything but the workspace).
+dsfp8_status grouped_args(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
+                          int64_t as_kb_stride, const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
+                          const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* C,
+                          int64_t ldc, int scale_fmt, dsfp8::GemmArgs& a) {
   if (!dim_ok(M_total) || !dim_ok(N) || !dim_ok(K)) return DSFP8_ERR_SHAPE;
   if (scale_fmt != DSFP8_SCALE_FP32 && scale_fmt != DSFP8_SCALE_UE8M0) return DSFP8_ERR_SCALE_FMT;
   if (E < 1 || E > kMaxExperts) return DSFP8_ERR_SHAPE;
@@ -256,11 +259,7 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   DSFP8_TRY(check_mat(B, E * N, K, ldb, 1));
   DSFP8_TRY(check_mat(b_s, E * nblk(N), nblk(K), ldbs, 4));
   DSFP8_TRY(check_mat(C, M_total, N, ldc, 2));
-  const size_t need = dsfp8_grouped_gemm_workspace_bytes(E, M_total, N, K);
-  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
-  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
-  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
-  dsfp8::GemmArgs a{};
+  a = dsfp8::GemmArgs{};
   a.A = static_cast<const uint8_t*>(A);
   a.lda = lda;
   a.a_s = a_s;
@@ -277,9 +276,38 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   a.K = K;
   a.offsets = offsets;
   a.E = E;
-  a.tile_start = static_cast<int32_t*>(workspace);
   a.pow2 = scale_fmt == DSFP8_SCALE_UE8M0;
+  return DSFP8_OK;
+}
+
+}  // namespace
+
+dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
+                                int64_t as_kb_stride, const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
+                                const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* C,
+                                int64_t ldc, int scale_fmt, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  dsfp8::GemmArgs a;
+  DSFP8_TRY(grouped_args(A, lda, a_s, as_row_stride, as_kb_stride, B, ldb, b_s, ldbs, offsets, E, M_total, N, K, C,
+                         ldc, scale_fmt, a));
+  const size_t need = dsfp8_grouped_gemm_workspace_bytes(E, M_total, N, K);
+  if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
+  if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
+  if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
+  a.tile_start = static_cast<int32_t*>(workspace);
   return launched(dsfp8::launch_grouped_gemm(a, stream));
+}
+
+dsfp8_status dsfp8_grouped_gemm_noalloc(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
+                                        int64_t as_kb_stride, const void* B, int64_t ldb, const float* b_s,
+                                        int64_t ldbs, const int32_t* offsets, int64_t E, int64_t M_total, int64_t N,
+                                        int64_t K, void* C, int64_t ldc, int scale_fmt, hipStream_t stream) {
+  dsfp8::GemmArgs a;
+  DSFP8_TRY(grouped_args(A, lda, a_s, as_row_stride, as_kb_stride, B, ldb, b_s, ldbs, offsets, E, M_total, N, K, C,
+                         ldc, scale_fmt, a));
+  if (E > DSFP8_NOALLOC_MAX_EXPERTS) return DSFP8_ERR_SCRATCH;
+  static_assert(DSFP8_NOALLOC_MAX_EXPERTS == dsfp8::kNoAllocMaxExperts, "header and library agree");
+  return launched(dsfp8::launch_grouped_gemm_noalloc(a, stream));
 }
 
 namespace {

@@ -25,6 +25,8 @@
 // skinny_gemm_kernel for decode rows; grouped_merged_kernel for the
 // per-expert products (three tile heights in one launch, scheduled by
 // tile_schedule_kernel from the device-side offsets).
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -1665,3 +1667,48 @@ size_t grouped_workspace_bytes(int64_t E) {
 
 }  // namespace dsfp8
 
+// ---- allocation-free grouped product ------------------------------------------
+//
+// The grouped product's only scratch is the tile schedule (kMaxClasses
+// int32 rows of E + 1 entries).  For callers that cannot allocate, it lives
+// in this static device array instead of a caller workspace; every GPU the
+// library runs on holds its own copy (zero-initialised at load, kept until
+// the process ends).  Host code never passes the array's name to a kernel:
+// the name is a host-side stand-in, so the device address is looked up once
+// per device with hipGetSymbolAddress and that pointer is used instead.
+static __device__ __align__(256) int32_t scratch[dsfp8::kMaxClasses * (dsfp8::kNoAllocMaxExperts + 1)];
+
+namespace dsfp8 {
+
+hipError_t noalloc_scratch(int32_t** out) {
+  constexpr int kDevices = 64;
+  static std::atomic<int32_t*> cache[kDevices];
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  int32_t* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Called with device `dev` current; two threads racing here both store
+    // the same address.
+    void* q = nullptr;
+    err = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (q == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<int32_t*>(q);
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_grouped_gemm_noalloc(GemmArgs a, hipStream_t stream) {
+  if (a.E > kNoAllocMaxExperts) return hipErrorInvalidValue;  // checked by the caller first
+  int32_t* p = nullptr;
+  const hipError_t err = noalloc_scratch(&p);
+  if (err != hipSuccess) return err;
+  a.tile_start = p;
+  return launch_grouped_gemm(a, stream);
+}
+
+}  // namespace dsfp8

@@ -135,6 +135,13 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 
 size_t grouped_workspace_bytes(int64_t E);
 
+// The grouped product with its tile schedule in a static device array of
+// 3 * (kNoAllocMaxExperts + 1) int32 per GPU instead of a caller workspace
+// (for callers that cannot allocate).  Calls that overlap on one GPU share
+// the array and race.
+constexpr int64_t kNoAllocMaxExperts = 4096;
+hipError_t launch_grouped_gemm_noalloc(GemmArgs a, hipStream_t stream);
+
 // Number of K splits the dense product uses for this shape (1 = none), and the
 // fp32 workspace that requires.  Small products (few output tiles) split their
 // K-blocks over several workgroups so that the weight streams from every CU.

@@ -4,9 +4,10 @@
  * C ABI of libdsfp8.so.  Every entry point takes plain device pointers and
  * sizes, enqueues its kernels on the caller's HIP stream and returns without
  * synchronising.  The library allocates no memory; all buffers are owned by
- * the caller.  Its only global state is a per-device cache of the
+ * the caller.  Its only global state is (1) a per-device cache of the
  * compute-unit count (read once with hipDeviceGetAttribute, used to size
- * grids).
+ * grids) and (2) the static device scratch of dsfp8_grouped_gemm_noalloc
+ * (one copy per GPU, with its address cached per device).
  *
  * Sources of the operations (the DeepSeek-V3 inference code as described by):
  *   [AG]  "DeepSeek-V3 Administrator & Developer Guide" (doccompiler.ai)
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSFP8_ABI_VERSION 5
+#define DSFP8_ABI_VERSION 6
 #define DSFP8_BLOCK 128
 
 typedef int dsfp8_status;
@@ -75,7 +76,9 @@ enum {
   DSFP8_ERR_WORKSPACE = -6,  /* workspace smaller than the size query returned    */
   DSFP8_ERR_LAUNCH = -7,     /* the HIP runtime reported a launch failure         */
   DSFP8_ERR_DTYPE = -8,      /* unknown input element type                        */
-  DSFP8_ERR_UNSUPPORTED = -9 /* a fused form does not support this operand layout */
+  DSFP8_ERR_UNSUPPORTED = -9, /* a fused form does not support this operand layout */
+  DSFP8_ERR_SCRATCH = -10     /* the problem exceeds the static scratch of a
+                                 *_noalloc entry point                            */
 };
 
 /* Scale formats.  UE8M0 rounds each scale value up to a power of two
@@ -241,6 +244,31 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K);
+
+/*
+ * dsfp8_grouped_gemm without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation).  It computes exactly what dsfp8_grouped_gemm computes,
+ * with the same kernels, so the two give bit-identical results.  The only
+ * scratch, the per-expert tile schedule, lives in a static device array of
+ * 3 * (DSFP8_NOALLOC_MAX_EXPERTS + 1) int32 (about 48 KB) that every GPU the
+ * library runs on holds until the process ends; no call allocates anything.
+ * Each call rewrites every schedule entry it reads before reading it, so no
+ * state carries over from earlier calls.  All calls on one GPU share that
+ * GPU's array: calls that may overlap in time on the same GPU (different
+ * streams without ordering between them) race and must not be issued.
+ * Arguments as for dsfp8_grouped_gemm.
+ * Errors: as dsfp8_grouped_gemm without WORKSPACE; SCRATCH when
+ * E > DSFP8_NOALLOC_MAX_EXPERTS (nothing launched); LAUNCH also when the
+ * scratch's device address cannot be obtained.
+ */
+#define DSFP8_NOALLOC_MAX_EXPERTS 4096
+dsfp8_status dsfp8_grouped_gemm_noalloc(const void* A, int64_t lda,
+                                        const float* a_s, int64_t as_row_stride, int64_t as_kb_stride,
+                                        const void* B, int64_t ldb, const float* b_s, int64_t ldbs,
+                                        const int32_t* offsets, int64_t E, int64_t M_total,
+                                        int64_t N, int64_t K, void* C, int64_t ldc, int scale_fmt,
+                                        hipStream_t stream);
 
 /*
  * Gated up-projection: the block-scaled FP8 product with the SiLU gate and

@@ -17,7 +17,7 @@ from block_scaled_fp8_act_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsfp8.h")
 
-OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE, UNSUP, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 P = 0x10000          # a fake, 256-byte aligned device address (never dereferenced)
 
 
@@ -49,7 +49,7 @@ def test_exports_every_declared_function(lib):
 
 def test_abi_version_and_strings(lib):
     assert lib.dsfp8_abi_version() == header_constant("#define DSFP8_ABI_VERSION")
-    for st in (OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE, UNSUP):
+    for st in (OK, NULL, SHAPE, LD, ALIGN, FMT, WS, LAUNCH, DTYPE, UNSUP, SCRATCH):
         s = lib.dsfp8_status_string(st)
         assert s and s != b"unknown status"
     assert lib.dsfp8_status_string(12345) == b"unknown status"
@@ -59,7 +59,7 @@ def test_status_codes_match_header():
     for name, v in [("DSFP8_ERR_NULL", NULL), ("DSFP8_ERR_SHAPE", SHAPE), ("DSFP8_ERR_LD", LD),
                     ("DSFP8_ERR_ALIGN", ALIGN), ("DSFP8_ERR_SCALE_FMT", FMT), ("DSFP8_ERR_WORKSPACE", WS),
                     ("DSFP8_ERR_LAUNCH", LAUNCH), ("DSFP8_ERR_DTYPE", DTYPE),
-                    ("DSFP8_ERR_UNSUPPORTED", UNSUP)]:
+                    ("DSFP8_ERR_UNSUPPORTED", UNSUP), ("DSFP8_ERR_SCRATCH", SCRATCH)]:
         assert header_constant(name) == v
 
 
@@ -154,6 +154,32 @@ def test_grouped_validation(lib):
     assert call(wsb=need - 1) == WS
     assert call(ws=None) == NULL
     assert lib.dsfp8_grouped_gemm_workspace_bytes(0, 1, 1, 1) == 0
+
+
+def test_grouped_noalloc_validation(lib):
+    g = lib.dsfp8_grouped_gemm_noalloc
+    names = ["A", "lda", "a_s", "as_rs", "as_ks", "B", "ldb", "b_s", "ldbs", "offsets", "E", "M", "N", "K", "C",
+             "ldc", "fmt", "stream"]
+    args = [P, 256, P, 1, 100, P, 256, P, 2, P, 4, 100, 64, 256, P, 64, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return g(*a)
+
+    limit = header_constant("#define DSFP8_NOALLOC_MAX_EXPERTS")
+    assert limit == 4096
+    assert call(fmt=3) == FMT
+    assert call(E=0) == SHAPE
+    assert call(E=70000) == SHAPE
+    assert call(E=limit + 1) == SCRATCH
+    assert call(offsets=None) == NULL
+    assert call(offsets=P + 2) == ALIGN
+    assert call(ldb=100) == LD
+    assert call(ldbs=1) == LD
+    assert call(as_ks=99) == LD
+    assert call(A=None) == NULL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
