@@ -60,7 +60,7 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // ---- block scale ---------------------------------------------------------------
 
 // Scale of a block from its absolute maximum: max(amax, 1e-4) / 448 as a
-// correctly rounded fp32 division, optionally rounded up to a power of two
+// correctly rounded fp32 division (any fp32 amax), optionally rounded up to a power of two
 // (ue8m0).  The power-of-two rounding works on the bits: a positive normal
 // value with a non-zero fraction moves to the next binade with a zero
 // fraction, which is exactly the smallest power of two not below it.
@@ -72,6 +72,25 @@ __device__ __forceinline__ float block_scale(float amax, bool ue8m0) {
     s = __uint_as_float(u);
   }
   return s;
+}
+
+// The same scale for a block maximum that is a bf16 value (an activation, or
+// the gate's bf16 output) with two fp32 operations fewer: max(amax, 1e-4) / 448
+// as one multiply by RN(1/448) and one correction (div_by_scale below).  For
+// every bf16 amax and the clamp constant this equals the correctly rounded
+// division (an exact rational check over all bf16 significands on the CPU;
+// every intermediate stays normal, so one binade covers all exponents).
+__device__ __forceinline__ float block_scale_bf16(float amax, bool ue8m0);
+
+// RN(1/s) for a scale produced by block_scale_bf16: the hardware reciprocal
+// (within one ulp) refined by one Newton step with an fma residual,
+// e = 1 - s*r0 and r = r0 + r0*e.  For every such s, and every r0 within two
+// ulp of 1/s, the result is the correctly rounded reciprocal (exact rational
+// check on the CPU over all reachable scale significands).
+__device__ __forceinline__ float recip_rn(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(r0, e, r0);
 }
 
 // x / s, correctly rounded, given r = RN(1/s): q = RN(x*r), then one
@@ -89,6 +108,17 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   float q = x * r;
   float t = __builtin_fmaf(q, s, -x);
   return __builtin_fmaf(-t, r, q);
+}
+
+__device__ __forceinline__ float block_scale_bf16(float amax, bool ue8m0) {
+  constexpr float kRecip448 = 1.0f / kE4m3Max;  // RN(1/448), folded at compile time
+  float s = div_by_scale(fmaxf(amax, kScaleFloor), kE4m3Max, kRecip448);
+  if (ue8m0) {
+    uint32_t u = __float_as_uint(s);
+    if (u & 0x007fffffu) u = (u + 0x00800000u) & 0xff800000u;
+    s = __uint_as_float(u);
+  }
+  return s;
 }
 
 // ---- division by a launch constant ------------------------------------------------

@@ -396,8 +396,8 @@ __device__ __forceinline__ void store_glu_quant(const GemmArgs& p, const TileRef
       amax = fmaxf(amax, fabsf(v[j]));
     }
     amax = max_row16(amax);
-    const float sc = block_scale(amax, p.q_ue8m0);
-    const float rc = 1.0f / sc;
+    const float sc = block_scale_bf16(amax, p.q_ue8m0);
+    const float rc = recip_rn(sc);
     const int64_t row = t.row0 + r;
     if (row < t.row_end) {
       u32x2 o;

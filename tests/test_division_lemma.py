@@ -62,3 +62,66 @@ def test_corrected_quotient_is_correctly_rounded():
                     if q1 != rn32(xx / s):
                         bad.append((s, xx))
     assert not bad, bad[:5]
+
+
+def _f32(x):
+    """The fp32 value of a Fraction that is representable (checked)."""
+    v = np.float32(float(x))
+    assert Fraction(float(v)) == x
+    return v
+
+
+def _neighbours(y, k):
+    """The fp32 values within k units in the last place of fp32 y (y > 0)."""
+    out = [np.float32(y)]
+    lo = hi = np.float32(y)
+    for _ in range(k):
+        lo = np.nextafter(lo, np.float32(0))
+        hi = np.nextafter(hi, np.float32(np.inf))
+        out += [lo, hi]
+    return [Fraction(float(v)) for v in out]
+
+
+# Every block maximum the quantisers meet is a bf16 value (the input, or the
+# gate's bf16 output) or the clamp constant fl(1e-4); by scale invariance
+# (every intermediate below stays normal for a >= 1e-4) one binade of bf16
+# significands covers them all.
+_AMAXES = [Fraction(128 + m, 128) for m in range(128)] + [Fraction(float(np.float32(1e-4)))]
+
+
+def test_scale_by_reciprocal_and_correction():
+    """s = RN(a / 448) computed as q = RN(a * r), t = RN(q * 448 - a) (fma,
+    exact), s = RN(q - t * r) with r = RN(1 / 448)."""
+    r = rn32(Fraction(1, 448))
+    bad = []
+    for a in _AMAXES:
+        q = rn32(a * r)
+        t = rn32(q * 448 - a)
+        assert t == q * 448 - a          # the fma residual is exact
+        s = rn32(q - t * r)
+        if s != rn32(a / 448):
+            bad.append(a)
+    assert not bad, bad[:5]
+
+
+def test_reciprocal_refinement():
+    """RN(1 / s) for every scale s the quantisers can produce (fp32 scales
+    RN(a / 448) and power-of-two scales), computed as r0 = the hardware
+    reciprocal, e = RN(1 - s * r0) (fma), r = RN(r0 + r0 * e) (fma): correct
+    for every r0 within two units in the last place of 1/s (the hardware
+    reciprocal is specified to within one)."""
+    scales = {rn32(a / 448) for a in _AMAXES} | {Fraction(1)}
+    bad = []
+    for s in scales:
+        # scale to [1, 2): the refinement is invariant under powers of two
+        while s >= 2:
+            s /= 2
+        while s < 1:
+            s *= 2
+        want = rn32(1 / s)
+        for r0 in _neighbours(_f32(want), 2):
+            e = rn32(1 - s * r0)
+            r = rn32(r0 + r0 * e)
+            if r != want:
+                bad.append((s, r0))
+    assert not bad, bad[:5]
