@@ -502,7 +502,7 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
     lib = ds._lib.load()
     code = 1 if fmt == "ue8m0" else 0
     wsb = lib.dsfp8_gemm_workspace_bytes(M, N, K)
-    wsbuf = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    wsbuf = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)  # zero-filled once (arrival counters)
     srs, sks = xs.stride(0), xs.stride(1)
 
     def aq_call(i, stream):

@@ -199,7 +199,8 @@ def gemm(a, a_s, b, b_s, out=None, scale_fmt="fp32"):
     lib = _lib.load()
     c = _out(out, (M, N), torch.bfloat16, a.device, "out")
     wsb = lib.dsfp8_gemm_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device) if wsb else None
+    # zero-filled, as the split products' arrival counters require
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=a.device) if wsb else None
     st = lib.dsfp8_gemm(a.data_ptr(), _ld(a), a_s.data_ptr(), ars, aks, b.data_ptr(), _ld(b), b_s.data_ptr(),
                         _ld(b_s), c.data_ptr(), _ld(c), M, N, K, _fmt(scale_fmt),
                         ws.data_ptr() if ws is not None else None, wsb, _stream(a))

@@ -1197,6 +1197,201 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
   if (r < p.M && n0 + c < p.N) p.C[(int64_t)r * p.ldc + n0 + c] = __builtin_bit_cast(uint16_t, (__bf16)sum);
 }
 
+// ---- small products in one launch ------------------------------------------------
+//
+// Products with few output tiles (decode rows, the ragged shape) are bound by
+// latency, not by bandwidth or the matrix cores.  gemm_rd_kernel gives each
+// workgroup of kRdWaves waves one 16FM x 16FN output tile and a range of
+// K-blocks; wave w takes the range's K-blocks w, w + kRdWaves, ... (at most
+// kRdDepth of them) and loads all of its MFMA operands straight from memory
+// into registers at once, so a workgroup needs one memory round trip.  Each
+// K-block's partial product is rescaled into fp32 accumulators as in the
+// large kernels (the weight fragment is the MFMA's first operand, so a lane's
+// four results are four columns of one row and share one activation scale);
+// the waves' sums are then added in wave order through LDS.  When a tile's
+// K-blocks are split over several workgroups, each writes its fp32 sum to the
+// workspace and increments the tile's arrival counter; the workgroup that
+// arrives last adds all the sums in split order (the result does not depend
+// on which one that is) and stores bf16, then clears the counter for the next
+// call.  One launch, deterministic.  All accesses go through buffer
+// resources: a lane with nothing to load passes an offset past the
+// resource's end and reads zero.
+
+constexpr int kRdWaves = 8;
+constexpr int kRdDepth = 2;
+
+struct RdPlan {
+  int32_t tiles_m, tiles_n, splits, per;  // per: K-blocks per split
+  int32_t nkb;
+  uint32_t a_bytes, b_bytes, as_bytes;    // extents of A, B and the activation scales
+  int32_t* counters;                      // [tiles], zero between calls (splits > 1)
+  float* partials;                        // [splits][tiles][16FM * 16FN] (splits > 1)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rd_buffer(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+// 32 bytes of one operand row for a lane (bytes k .. k + 31 of the row at
+// byte offset `row`, or kOob for a row to skip); VEC-byte pieces at or past K
+// read as zero (VEC divides K).
+template <int VEC>
+__device__ __forceinline__ v8i rd_frag(__amdgpu_buffer_rsrc_t r, uint32_t row, uint32_t k, uint32_t K) {
+  v8i f;
+  if constexpr (VEC == 16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t kk = k + 16 * h;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (row != kOob && kk < K) ? row + kk : kOob, 0, 0);
+      f[4 * h] = v.x; f[4 * h + 1] = v.y; f[4 * h + 2] = v.z; f[4 * h + 3] = v.w;
+    }
+  } else {
+    static_assert(VEC == 8, "8- or 16-byte pieces");
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t kk = k + 8 * h;
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (row != kOob && kk < K) ? row + kk : kOob, 0, 0);
+      f[2 * h] = v.x; f[2 * h + 1] = v.y;
+    }
+  }
+  return f;
+}
+
+template <int FM, int FN, int VEC, bool POW2>
+__global__ __launch_bounds__(64 * kRdWaves) void gemm_rd_kernel(GemmArgs p, RdPlan q) {
+  constexpr int TM = 16 * FM, TN = 16 * FN, ELEMS = TM * TN;
+  static_assert(FM * FN <= kRdWaves && 128 % TN == 0, "a wave per subtile; a tile's columns in one 128-block");
+  __shared__ v4f red[kRdWaves][FM * FN][64];
+  __shared__ int last;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int fr = lane & 15, fg = lane >> 4;
+  const int tiles = q.tiles_m * q.tiles_n;
+  const int tile = (int)(blockIdx.x % (unsigned)tiles), split = (int)(blockIdx.x / (unsigned)tiles);
+  const int tm = tile % q.tiles_m, tn = tile / q.tiles_m;
+  const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
+  const uint32_t m0 = (uint32_t)tm * TM, n0 = (uint32_t)tn * TN;
+  const int kb_lo = split * q.per, kb_hi = kb_lo + q.per < q.nkb ? kb_lo + q.per : q.nkb;
+  const auto ra = rd_buffer(p.A, q.a_bytes);
+  const auto rb = rd_buffer(p.B, q.b_bytes);
+  const float* bsrow = p.b_s + (int64_t)(n0 / BK) * p.ldbs;
+
+  v8i bf[kRdDepth][FN], af[kRdDepth][FM];
+  float sa[kRdDepth][FM], sb[kRdDepth];
+  // the scales first (branch-free buffer loads: 0 for rows past M and
+  // K-blocks past the range), then the operands
+  const auto rsa = rd_buffer(p.a_s, q.as_bytes);
+#pragma unroll
+  for (int d = 0; d < kRdDepth; ++d) {
+    const int kb = kb_lo + wave + d * kRdWaves;
+    const bool live = kb < kb_hi;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t m = m0 + 16 * i + fr;
+      sa[d][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rsa, (live && m < M) ? (m * (uint32_t)p.as_rs + (uint32_t)kb * (uint32_t)p.as_ks) * 4 : kOob, 0, 0));
+    }
+    sb[d] = live ? bsrow[kb] : 0.0f;
+  }
+#pragma unroll
+  for (int d = 0; d < kRdDepth; ++d) {
+    const int kb = kb_lo + wave + d * kRdWaves;
+    const bool live = kb < kb_hi;
+    const uint32_t k = (uint32_t)kb * BK + 32 * fg;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint32_t n = n0 + 16 * j + fr;
+      bf[d][j] = rd_frag<VEC>(rb, (live && n < N) ? n * (uint32_t)p.ldb : kOob, k, K);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t m = m0 + 16 * i + fr;
+      af[d][i] = rd_frag<VEC>(ra, (live && m < M) ? m * (uint32_t)p.lda : kOob, k, K);
+    }
+  }
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int d = 0; d < kRdDepth; ++d) {
+    if (kb_lo + wave + d * kRdWaves >= kb_hi) break;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (POW2) {
+        // a row past M carries scale 0 (2^-127) times a zero fragment
+        const int ea = (int)(__float_as_uint(sa[d][i]) >> 23), eb = (int)(__float_as_uint(sb[d]) >> 23);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d][j], af[d][i], acc[i][j], 0, 0, 0, eb, 0, ea);
+      } else {
+        const float sc = sa[d][i] * sb[d];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[d][j], af[d][i],
+                                                                            v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc, acc[i][j][v]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) red[wave][i * FN + j][lane] = acc[i][j];
+  __syncthreads();
+  // Wave w < FM*FN finishes subtile w = (i, j): the waves' sums of its four
+  // outputs per lane (row 16i + fr, columns 16j + 4fg .. +3) added in wave
+  // order, each lane reading 16 consecutive bytes (no bank conflicts).
+  const bool owner = wave < FM * FN;
+  const int si = wave / FN, sj = wave % FN;
+  v4f sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (owner) {
+    sum = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kRdWaves; ++w) sum += red[w][wave][lane];
+  }
+  if (q.splits > 1) {
+    // The sums, the counter and the final reads are device-scope atomic
+    // accesses, which the hardware keeps coherent across the XCDs' separate
+    // L2 caches without writing back or invalidating them (a device-scope
+    // fence would do both, for the whole cache, in every workgroup).  The
+    // stores are complete (vmcnt 0) before the workgroup's arrival counts.
+    const int64_t slot = ((int64_t)tile * FM * FN + wave) * 64 + lane;   // within one split's block
+    const int64_t split_elems = (int64_t)tiles * ELEMS;
+    if (owner) {
+      float* mine = q.partials + split * split_elems + slot * 4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) __hip_atomic_store(mine + v, sum[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(q.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == q.splits - 1;
+    __syncthreads();
+    if (!last) return;
+    if (owner) {
+      sum = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sp = 0; sp < q.splits; ++sp) {
+        const float* src = q.partials + sp * split_elems + slot * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(q.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!owner) return;
+  const uint32_t row = m0 + 16 * si + fr, col = n0 + 16 * sj + 4 * fg;
+  if (row < M) {
+    uint16_t* dst = p.C + (int64_t)row * p.ldc + col;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (col + v < N) dst[v] = __builtin_bit_cast(uint16_t, (__bf16)sum[v]);
+  }
+}
+
 // Expert row range [lo, hi) with every bound clamped into [0, M_total].
 __device__ __forceinline__ void expert_rows(const int32_t* offsets, int64_t e, int64_t M, int64_t& lo, int64_t& hi) {
   int64_t a = offsets[e], b = offsets[e + 1];
@@ -1500,9 +1695,77 @@ int gemm_k_splits(int64_t M, int64_t N, int64_t K) {
   return (int)((nkb + per - 1) / per);     // no empty split
 }
 
+// Tile shape and K split of the one-launch small-product kernel: 32-row tiles
+// for at most 32 rows, else 64; 64 columns (32 when that leaves fewer than
+// 256 workgroups); one K-block per wave when one workgroup covers K, else two
+// per wave (fewer splits: decode 32x1536x7168 9.9 against 11.2 us, 64x4096x7168
+// 20.4 against 25.1 us; three or four per wave were slower on the decode
+// shape).
+struct RdShape {
+  int fm, fn;
+  int64_t tiles_m, tiles_n, splits, per, nkb;
+};
+
+RdShape rd_shape(int64_t M, int64_t N, int64_t K) {
+  RdShape r{};
+  r.nkb = (K + BK - 1) / BK;
+  r.fm = M <= 32 ? 2 : 4;
+  auto make = [&](int fn) {
+    r.fn = fn;
+    r.tiles_m = (M + 16 * r.fm - 1) / (16 * r.fm);
+    r.tiles_n = (N + 16 * fn - 1) / (16 * fn);
+    r.per = kRdWaves;
+    r.splits = (r.nkb + r.per - 1) / r.per;
+    if (r.splits > 1) {
+      r.per = kRdWaves * kRdDepth;
+      r.splits = (r.nkb + r.per - 1) / r.per;
+    }
+  };
+  make(r.fm == 4 ? 2 : 4);
+  if (r.fm == 2 && r.tiles_m * r.tiles_n * r.splits < 256) make(2);
+  return r;
+}
+
+// Workspace of a split product: the one-launch kernel's arrival counters
+// (one int per tile, 256-byte aligned area) first, then the fp32 partial
+// sums of whichever split form runs.
+size_t rd_counter_bytes(int64_t M, int64_t N, int64_t K) {
+  const RdShape r = rd_shape(M, N, K);
+  return ((size_t)(r.tiles_m * r.tiles_n) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int s = gemm_k_splits(M, N, K);
-  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+  if (s <= 1) return 0;
+  const RdShape r = rd_shape(M, N, K);
+  const size_t rd = r.splits > 1 ? (size_t)(r.splits * r.tiles_m * r.tiles_n) * 256 * r.fm * r.fn * sizeof(float) : 0;
+  const size_t old = (size_t)s * (size_t)M * (size_t)N * sizeof(float);
+  return rd_counter_bytes(M, N, K) + (rd > old ? rd : old);
+}
+
+// The one-launch kernel needs 8-byte pieces of A and B rows (K, lda, ldb
+// multiples of 8, 8-byte aligned operands) and 32-bit offsets; returns the
+// piece width (16 or 8), or 0 if it does not apply.
+int rd_vec(const GemmArgs& a) {
+  const int64_t lim = (int64_t)1 << 31;
+  if ((a.M - 1) * a.lda + a.K >= lim || (a.N - 1) * a.ldb + a.K >= lim) return 0;
+  if (((a.M - 1) * a.as_rs + ((a.K + BK - 1) / BK - 1) * a.as_ks + 1) * 4 >= lim) return 0;
+  if (a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16)) return 16;
+  if (a.K % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 && aligned(a.A, 8) && aligned(a.B, 8)) return 8;
+  return 0;
+}
+
+template <int FM, int FN>
+hipError_t launch_rd(const GemmArgs& a, const RdPlan& q, int vec, dim3 grid, hipStream_t stream) {
+  const dim3 blk(64 * kRdWaves);
+  if (vec == 16) {
+    if (a.pow2) hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 16, true>), grid, blk, 0, stream, a, q);
+    else hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 16, false>), grid, blk, 0, stream, a, q);
+  } else {
+    if (a.pow2) hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 8, true>), grid, blk, 0, stream, a, q);
+    else hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 8, false>), grid, blk, 0, stream, a, q);
+  }
+  return hipGetLastError();
 }
 
 // The skinny kernel loads 16-byte chunks of A and B rows.  Measured against
@@ -1513,6 +1776,33 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 bool skinny_ok(const GemmArgs& a) {
   const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && a.N > kSkinny32MinN && a.N <= kSkinny32MaxN);
   return rows && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16);
+}
+
+// Split K over workgroups for operands the one-launch kernel does not take:
+// fp32 partials [splits, M, N] in a.partial, summed in split order by a
+// second kernel.
+hipError_t launch_gemm_splitk(const GemmArgs& a, int splits, hipStream_t stream) {
+  static_assert(CfgDma::BM == Cfg128::BM && CfgDma::BN == Cfg128::BN, "same split grid for both pipelines");
+  dim3 g = dense_grid<CfgDma>(a);
+  g.y = (unsigned)splits;
+  hipError_t err;
+  if (a.M <= CfgGrp::BM && pick_vec<CfgGrp>(a) <= 0) {
+    // at most 64 rows: the 64-row tiles (same grid, one row tile)
+    static_assert(CfgGrp::BN == CfgDma::BN, "same column tiles");
+    DSFP8_LAUNCH_DMA(gemm_kernel, CfgGrp, false, g, stream, a);
+    err = hipGetLastError();
+  } else {
+    err = dispatch<CfgDma, Cfg128, false>(a, g, g, stream);
+  }
+  if (err != hipSuccess) return err;
+  if (splits > 8) {
+    const int64_t groups = (a.M * a.N + 255) / 256;
+    hipLaunchKernelGGL((splitk_reduce_kernel<1, 32>), dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
+  } else {
+    const int64_t groups = (a.M * a.N + 1023) / 1024;
+    hipLaunchKernelGGL((splitk_reduce_kernel<4, 8>), dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
@@ -1530,27 +1820,31 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   const int splits = gemm_k_splits(a.M, a.N, a.K);
   if (splits > 1 && a.partial != nullptr) {
-    static_assert(CfgDma::BM == Cfg128::BM && CfgDma::BN == Cfg128::BN, "same split grid for both pipelines");
-    dim3 g = dense_grid<CfgDma>(a);
-    g.y = (unsigned)splits;
-    hipError_t err;
-    if (a.M <= CfgGrp::BM && pick_vec<CfgGrp>(a) <= 0) {
-      // at most 64 rows: the 64-row tiles (same grid, one row tile)
-      static_assert(CfgGrp::BN == CfgDma::BN, "same column tiles");
-      DSFP8_LAUNCH_DMA(gemm_kernel, CfgGrp, false, g, stream, a);
-      err = hipGetLastError();
-    } else {
-      err = dispatch<CfgDma, Cfg128, false>(a, g, g, stream);
+    // the workspace starts with the one-launch kernel's counters
+    uint8_t* ws = reinterpret_cast<uint8_t*>(a.partial);
+    const size_t cbytes = rd_counter_bytes(a.M, a.N, a.K);
+    const int vec = rd_vec(a);
+    if (vec > 0) {
+      const RdShape r = rd_shape(a.M, a.N, a.K);
+      RdPlan q;
+      q.tiles_m = (int32_t)r.tiles_m;
+      q.tiles_n = (int32_t)r.tiles_n;
+      q.splits = (int32_t)r.splits;
+      q.per = (int32_t)r.per;
+      q.nkb = (int32_t)r.nkb;
+      q.a_bytes = (uint32_t)((a.M - 1) * a.lda + a.K);
+      q.b_bytes = (uint32_t)((a.N - 1) * a.ldb + a.K);
+      q.as_bytes = (uint32_t)(((a.M - 1) * a.as_rs + ((a.K + BK - 1) / BK - 1) * a.as_ks + 1) * 4);
+      q.counters = reinterpret_cast<int32_t*>(ws);
+      q.partials = reinterpret_cast<float*>(ws + cbytes);
+      const dim3 grid((unsigned)(r.tiles_m * r.tiles_n * r.splits));
+      if (r.fm == 2 && r.fn == 4) return launch_rd<2, 4>(a, q, vec, grid, stream);
+      if (r.fm == 2) return launch_rd<2, 2>(a, q, vec, grid, stream);
+      return launch_rd<4, 2>(a, q, vec, grid, stream);
     }
-    if (err != hipSuccess) return err;
-    if (splits > 8) {
-      const int64_t groups = (a.M * a.N + 255) / 256;
-      hipLaunchKernelGGL((splitk_reduce_kernel<1, 32>), dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
-    } else {
-      const int64_t groups = (a.M * a.N + 1023) / 1024;
-      hipLaunchKernelGGL((splitk_reduce_kernel<4, 8>), dim3((unsigned)groups), dim3(256), 0, stream, a, splits);
-    }
-    return hipGetLastError();
+    GemmArgs b = a;
+    b.partial = reinterpret_cast<float*>(ws + cbytes);
+    return launch_gemm_splitk(b, splits, stream);
   }
   const int64_t big_tiles = ((a.M + CfgDmaBig::BM - 1) / CfgDmaBig::BM) * ((a.N + CfgDmaBig::BN - 1) / CfgDmaBig::BN);
   if (a.M >= CfgDmaBig::BM && big_tiles >= device_cu_count() && pick_vec<CfgDmaBig>(a) <= 0) {

@@ -400,6 +400,62 @@ __global__ __launch_bounds__(kThreads) void weight_dequant_kernel(DequantArgs a)
   }
 }
 
+// The same kernel for aligned operands whose extents fit 32-bit byte
+// offsets, through buffer resources (no per-lane branches, 32-bit address
+// arithmetic; a lane past N or K passes an offset past the resource's end),
+// with kDqLeanRows rows per workgroup: 69.5 us against 71.3 us for the
+// general kernel on [18432, 7168] (2 rows measured faster than 4, 8 slower;
+// plain instead of nontemporal stores 5% slower).  Bit-identical results.
+constexpr int kDqLeanRows = 2;
+
+__global__ __launch_bounds__(kThreads) void weight_dequant_lean_kernel(DequantArgs a, uint32_t wbytes, uint32_t sbytes,
+                                                                       uint32_t obytes) {
+  constexpr int kNt = 2;
+  const auto rw = buffer_of(a.w, wbytes);
+  const auto rs = buffer_of(a.S, sbytes);
+  const auto ro = buffer_of(a.out, obytes);
+  const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
+  const uint32_t ldw = (uint32_t)a.ldw, ldS = (uint32_t)a.ldS, ldo = (uint32_t)a.ldo;
+  const uint32_t cbase = blockIdx.x * (kThreads * 16) + threadIdx.x * 8;
+  const uint32_t row0 = blockIdx.y * kDqLeanRows;
+  u32x2 w[2][kDqLeanRows];
+  float sc[2][kDqLeanRows];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t col = cbase + h * (kThreads * 8);
+#pragma unroll
+    for (int r = 0; r < kDqLeanRows; ++r) {
+      const uint32_t n = row0 + r;
+      const bool in = n < N && col < K;
+      sc[h][r] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rs, in ? ((n / kBlock) * ldS + col / kBlock) * 4 : kOffNone, 0, 0));
+      w[h][r] = __builtin_amdgcn_raw_buffer_load_b64(rw, in ? n * ldw + col : kOffNone, 0, kNt);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t col = cbase + h * (kThreads * 8);
+#pragma unroll
+    for (int r = 0; r < kDqLeanRows; ++r) {
+      const uint32_t n = row0 + r;
+      const bool in = n < N && col < K;
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const float s = sc[h][r];
+      const uint32_t words[2] = {w[h][r].x, w[h][r].y};
+      uint32_t out[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], false);
+        f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], true);
+        out[2 * i] = pack_bf16x2(lo[0] * s, lo[1] * s);
+        out[2 * i + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(mk4(out[0], out[1], out[2], out[3]), ro,
+                                             in ? (n * ldo + col) * 2 : kOffNone, 0, kNt);
+    }
+  }
+}
+
 inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 }  // namespace
@@ -465,6 +521,15 @@ hipError_t launch_weight_dequant(const DequantArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.K == 0) return hipSuccess;
   const bool vec = (a.K % 16 == 0) && aligned(a.w, 16) && (a.ldw % 16 == 0) && aligned(a.out, 16) &&
                    (a.ldo % 8 == 0);
+  const int64_t wb = (a.N - 1) * a.ldw + a.K, ob = ((a.N - 1) * a.ldo + a.K) * 2;
+  const int64_t sb = (((a.N - 1) / kBlock) * a.ldS + (a.K - 1) / kBlock + 1) * 4;
+  const int64_t lim = (int64_t)1 << 31;
+  if (vec && wb < lim && ob < lim && sb < lim) {
+    dim3 g2((unsigned)((a.K + kThreads * 16 - 1) / (kThreads * 16)), (unsigned)((a.N + kDqLeanRows - 1) / kDqLeanRows));
+    hipLaunchKernelGGL(weight_dequant_lean_kernel, g2, dim3(kThreads), 0, stream, a, (uint32_t)wb, (uint32_t)sb,
+                       (uint32_t)ob);
+    return hipGetLastError();
+  }
   dim3 g((unsigned)((a.K + kThreads * 16 - 1) / (kThreads * 16)), (unsigned)((a.N + kDqRows - 1) / kDqRows));
   dim3 blk(kThreads);
   if (vec) hipLaunchKernelGGL((weight_dequant_kernel<true>), g, blk, 0, stream, a);

@@ -199,7 +199,14 @@ dsfp8_status dsfp8_weight_dequant(const void* w, int64_t N, int64_t K, int64_t l
  *          done inside the matrix instruction (CDNA4's block-scaled MFMA).
  *          The result definition is the same.
  *   workspace / workspace_bytes: scratch of at least
- *          dsfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
+ *          dsfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that
+ *          is 0), 16-byte aligned.  It must hold zeros before the first call
+ *          that uses it (allocate it zero-filled, or clear it once); every
+ *          call leaves it so again (the products that split K keep per-tile
+ *          arrival counters at its start and clear them when they finish), so
+ *          one workspace serves any later calls, of any shape, without being
+ *          cleared again.  Calls that may run at the same time must not share
+ *          a workspace.
  * Errors: NULL, SHAPE, LD, ALIGN, SCALE_FMT, WORKSPACE, LAUNCH.
  */
 dsfp8_status dsfp8_gemm(const void* A, int64_t lda,

@@ -121,9 +121,10 @@ def test_gemm_validation(lib):
     assert g(P, 256, P + 1, 2, 1, P, 256, P, 2, P, 64, 8, 64, 256, None, 0, None) == ALIGN
     assert g(P, 256, P, 2, 1, P, 256, P, 2, P + 1, 64, 8, 64, 256, None, 0, None) == ALIGN
     assert lib.dsfp8_gemm_workspace_bytes(4096, 18432, 7168) == 0
-    # a decode-shaped product splits K and needs an fp32 workspace
+    # a decode-shaped product splits K and needs a workspace: 256-byte aligned
+    # arrival counters, then fp32 partial sums of the output
     need = lib.dsfp8_gemm_workspace_bytes(32, 1536, 7168)
-    assert need > 0 and need % (32 * 1536 * 4) == 0
+    assert need >= 256 + 2 * 32 * 1536 * 4 and need % 4 == 0
     assert g(P, 7168, P, 1, 32, P, 7168, P, 56, P, 1536, 32, 1536, 7168, None, 0, None) == WS
     assert g(P, 7168, P, 1, 32, P, 7168, P, 56, P, 1536, 32, 1536, 7168, None, need, None) == NULL
     assert g(P, 7168, P, 1, 32, P, 7168, P, 56, P, 1536, 32, 1536, 7168, P + 4, need, None) == ALIGN

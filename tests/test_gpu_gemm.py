@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import block_scaled_fp8_act_amd as ds
+from block_scaled_fp8_act_amd import _lib
 from block_scaled_fp8_act_amd import inputs as I
 from oracle import formats as F
 from oracle import gemm as G
@@ -223,3 +224,35 @@ def test_dense_ffn_up_stacked_sampled():
 
 def test_dense_ffn_down_sampled():
     _sampled_product(4096, 7168, 18432, 70, 128, 3)
+
+
+@pytest.mark.parametrize("shapes", [
+    [(32, 1536, 7168), (32, 1536, 7168), (333, 2500, 1000), (100, 1000, 4096), (32, 1536, 7168)],
+    [(64, 300, 400), (257, 384, 640), (17, 300, 1536), (64, 300, 400)],
+])
+def test_split_products_reuse_one_workspace(shapes):
+    """Products that split K over workgroups keep per-tile arrival counters at
+    the start of the workspace and clear them when they finish: one workspace,
+    zero-filled once, serves a sequence of calls of different shapes, and a
+    repeated call gives the same bits (the last workgroup to arrive adds the
+    splits in split order, whichever it is).  The output is filled with a
+    sentinel before each call, so a call that found a counter not cleared
+    (and so never stored) would show."""
+    lib = _lib.load()
+    need = max(lib.dsfp8_gemm_workspace_bytes(M, N, K) for M, N, K in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    first = {}
+    for i, (M, N, K) in enumerate(shapes):
+        a, a_s, b, b_s = operands(M, N, K, I.TINY)
+        A, AS, B, BS = dev_u8(a), dev_scales(a_s, "kb"), dev_u8(b), dev_f32(b_s)
+        c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        st = lib.dsfp8_gemm(A.data_ptr(), K, AS.data_ptr(), AS.stride(0), AS.stride(1), B.data_ptr(), K,
+                            BS.data_ptr(), BS.stride(0), c.data_ptr(), N, M, N, K, 0, ws.data_ptr(), need, stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        got = host_bits16(c)
+        check_gemm_full(got, a, a_s, b, b_s, f"call {i}: {M}x{N}x{K}")
+        if (M, N, K) in first:
+            assert np.array_equal(got, first[(M, N, K)]), f"call {i}: repeated {M}x{N}x{K} differs"
+        first.setdefault((M, N, K), got)
