@@ -613,6 +613,12 @@ def only(kernel, reps, dev, fmt="fp32"):
     if kernel == "routed_experts":
         print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps)}))
         return
+    if kernel == "small_products":
+        res = {"decode_qa": bench_small_gemm(dev, reps, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True),
+               "ragged_ue8m0": bench_small_gemm(dev, reps, "ragged ue8m0: 333x2500x1000", 333, 2500, 1000, "ue8m0",
+                                                False)}
+        print(json.dumps({"only": kernel, "reps": reps, "result": res}))
+        return
     if kernel == "copy":
         # calibration: a plain 1 GiB device-to-device copy (1 GiB read, 1 GiB written)
         src = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
@@ -653,7 +659,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["act_quant", "weight_dequant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
-                                       "copy", "routed_experts"],
+                                       "copy", "routed_experts", "small_products"],
                     help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
                          "(for rocprofv3)")
     ap.add_argument("--reps", type=int, default=3)
