@@ -463,6 +463,14 @@ __device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, uint32_t voff
                : "memory", "m0");
 }
 
+// Four bytes per lane (for rows that are only 4-byte aligned).
+__device__ __forceinline__ void dma_b32(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // The same with the nontemporal hint: for weight panels that one tile
 // streams once (the short, wide tiles of the grouped and gated products).
 __device__ __forceinline__ void dma_b128_nt(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
@@ -1083,13 +1091,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 // Products with at most 16 rows (decode at small batch): the weight is
 // streamed once and every output needs all of K, so one workgroup of
 // kSkinnyWaves waves owns 16 output columns over the whole of K.  Its waves
-// take the K-blocks in turn (wave w: w, w + W, ...), load their MFMA operands
-// straight from memory into registers (kSkinnyDepth K-blocks in flight;
-// nontemporal loads of the weight measured 8% slower), and multiply the
-// 16-column weight fragment by the 16-row activation fragment per K-block;
-// the per-wave sums are then added in wave order through LDS and rounded to
-// bf16.  No split of K across workgroups, so no fp32 partials and no second
-// kernel.
+// take the K-blocks in turn (wave w: w, w + W, ...), kSkinnyDepth K-blocks in
+// flight: the weight's 16 rows of each K-block go straight to the wave's own
+// LDS slot as two 8-row, full-line segments (the large kernels' swizzled
+// layout), the activation fragments straight into registers; the wave then
+// multiplies the 16-column weight fragment by the 16-row activation fragment
+// per K-block.  The per-wave sums are added in wave order through LDS (the
+// staging slots again) and rounded to bf16.  No split of K across
+// workgroups, so no fp32 partials and no second kernel.  Against loading the
+// weight fragment into registers (16 rows of 64 bytes per instruction, half
+// of each line): 1x7168x18432 26.5 against 28.9 us, 4x36864x7168 54.2
+// against 57.9, 8x1536x7168 7.0 against 8.3, 32x4096x7168 12.8 against
+// 13.6; 1x18432x7168 unchanged (29.4 us; 32.9 against 31.9 with ue8m0
+// scales).  Nontemporal loads of the weight measured 8% slower; a fourth
+// K-block per wave was no faster at one row and slower at 32.
 constexpr int kSkinnyWaves = 16;
 constexpr int kSkinnyDepth = 3;
 constexpr int kSkinnyRows = 16;
@@ -1116,9 +1131,14 @@ __device__ __forceinline__ v8i skinny_frag(const uint8_t* row, bool valid, int64
 
 // FRAGS 16-row activation fragments (up to 16 * FRAGS rows): each wave
 // multiplies its weight fragment by every activation fragment of a K-block.
+constexpr int kSkinnySlot = 16 * BK;  // one K-block of the 16 weight rows
+constexpr int kSkinnyLds = kSkinnyWaves * kSkinnyDepth * kSkinnySlot;
+
 template <bool POW2, int FRAGS>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs p) {
-  __shared__ float red[kSkinnyWaves][FRAGS][64][4];
+  static_assert(kSkinnyLds >= kSkinnyWaves * FRAGS * 64 * 16, "reduction area within the staging slots");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSkinnyLds];
+  float (*red)[FRAGS][64][4] = reinterpret_cast<float (*)[FRAGS][64][4]>(smem);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, fg = lane >> 4;
@@ -1126,11 +1146,18 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
   const int64_t K = p.K;
   const int64_t nk = (K + BK - 1) / BK;
   // Column layout (weight fragment first): lane (fr, fg) of fragment f ends
-  // with outputs C[16f + fr][n0 + 4fg + v]; it loads weight row n0 + fr and
-  // activation rows 16f + fr, bytes 32fg .. 32fg + 31 of each K-block.
-  const bool bv = n0 + fr < p.N;
-  const uint8_t* brow = p.B + (bv ? n0 + fr : 0) * p.ldb;
+  // with outputs C[16f + fr][n0 + 4fg + v]; it reads weight row n0 + fr from
+  // LDS and loads activation rows 16f + fr, bytes 32fg .. 32fg + 31 of each
+  // K-block.
   const float* bsr = p.b_s + (n0 / BK) * p.ldbs;
+  // The workgroup's weight rows under one descriptor (rows past N read as
+  // zero); lane -> LDS chunk lane % 8 of row 8h + lane / 8, which holds
+  // logical chunk dc[h] of that row.
+  const int64_t nrows = p.N - n0 < 16 ? p.N - n0 : 16;
+  const i32x4 rsb = make_rsrc(p.B + n0 * p.ldb, (uint32_t)((nrows - 1) * p.ldb + K));
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
+  const int dr = lane >> 3;
+  const uint32_t dc[2] = {(uint32_t)((lane & 7) ^ swz_key(dr)), (uint32_t)((lane & 7) ^ swz_key(dr + 8))};
   bool av[FRAGS];
   const uint8_t* arow[FRAGS];
   const float* asr[FRAGS];
@@ -1147,12 +1174,25 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
   for (int64_t kb0 = wave; kb0 < nk; kb0 += (int64_t)kSkinnyWaves * kSkinnyDepth) {
     v8i bf[kSkinnyDepth], af[kSkinnyDepth][FRAGS];
     float sa[kSkinnyDepth][FRAGS], sb[kSkinnyDepth];
+    // The previous pass's fragment reads from these slots have completed:
+    // their MFMAs have consumed them.
+#pragma unroll
+    for (int d = 0; d < kSkinnyDepth; ++d) {
+      const int64_t kb = kb0 + (int64_t)d * kSkinnyWaves;
+      if (kb >= nk) break;
+      const uint32_t slot = lds0 + (uint32_t)((wave * kSkinnyDepth + d) * kSkinnySlot);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t kk = (uint32_t)kb * BK + 16 * dc[h];
+        const bool ok = 8 * h + dr < nrows && kk < (uint32_t)K;
+        dma_b128(rsb, slot + (uint32_t)(h * 1024), ok ? (uint32_t)(8 * h + dr) * (uint32_t)p.ldb + kk : kOob, 0);
+      }
+    }
 #pragma unroll
     for (int d = 0; d < kSkinnyDepth; ++d) {
       const int64_t kb = kb0 + (int64_t)d * kSkinnyWaves;
       const bool live = kb < nk;
       const int64_t k = kb * BK + 32 * fg;
-      bf[d] = skinny_frag(brow, bv && live, k, K);
 #pragma unroll
       for (int f = 0; f < FRAGS; ++f) {
         af[d][f] = skinny_frag(arow[f], av[f] && live, k, K);
@@ -1160,6 +1200,11 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
       }
       sb[d] = live ? bsr[kb] : 0.0f;
     }
+    // this wave's own slots: its own loads complete (vmcnt 0) is enough
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int d = 0; d < kSkinnyDepth; ++d)
+      if (kb0 + (int64_t)d * kSkinnyWaves < nk) bf[d] = read_frag(smem + (wave * kSkinnyDepth + d) * kSkinnySlot, fr, fg);
 #pragma unroll
     for (int d = 0; d < kSkinnyDepth; ++d) {
       if (kb0 + (int64_t)d * kSkinnyWaves >= nk) break;
@@ -1181,6 +1226,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
       }
     }
   }
+  __syncthreads();  // every wave is done with its staging slots
 #pragma unroll
   for (int f = 0; f < FRAGS; ++f)
 #pragma unroll
@@ -1203,22 +1249,28 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
 // latency, not by bandwidth or the matrix cores.  gemm_rd_kernel gives each
 // workgroup of kRdWaves waves one 16FM x 16FN output tile and a range of
 // K-blocks; wave w takes the range's K-blocks w, w + kRdWaves, ... (at most
-// kRdDepth of them) and loads all of its MFMA operands straight from memory
-// into registers at once, so a workgroup needs one memory round trip.  Each
-// K-block's partial product is rescaled into fp32 accumulators as in the
-// large kernels (the weight fragment is the MFMA's first operand, so a lane's
-// four results are four columns of one row and share one activation scale);
-// the waves' sums are then added in wave order through LDS.  When a tile's
-// K-blocks are split over several workgroups, each writes its fp32 sum to the
-// workspace and increments the tile's arrival counter; the workgroup that
-// arrives last adds all the sums in split order (the result does not depend
-// on which one that is) and stores bf16, then clears the counter for the next
-// call.  One launch, deterministic.  All accesses go through buffer
-// resources: a lane with nothing to load passes an offset past the
-// resource's end and reads zero.
+// DEPTH of them) and issues all of their operand loads at once, so a
+// workgroup needs one memory round trip.  The loads go straight to LDS, each
+// wave into its own slots (one per K-block: the tile's A rows, then its B
+// rows, 128 bytes each in the swizzled layout of the large kernels), as full
+// 128-byte rows: 8 rows per 16-byte-per-lane instruction, or 2 rows per
+// 4-byte-per-lane instruction when the rows are only 8-byte aligned.  Loading
+// the MFMA operands straight into registers instead (16 rows of 64 bytes per
+// instruction, half of every 128-byte line) took 13-16% longer on the decode
+// shapes.  Each K-block's partial product is rescaled into fp32 accumulators
+// as in the large kernels (the weight fragment is the MFMA's first operand,
+// so a lane's four results are four columns of one row and share one
+// activation scale); the waves' sums are then added in wave order through
+// LDS (reusing the staging area).  When a tile's K-blocks are split over
+// several workgroups, each writes its fp32 sum to the workspace and
+// increments the tile's arrival counter; the workgroup that arrives last adds
+// all the sums in split order (the result does not depend on which one that
+// is) and stores bf16, then clears the counter for the next call.  One
+// launch, deterministic.  All accesses go through buffer resources: a lane
+// with nothing to load (a row past the matrix, bytes past K) passes an offset
+// past the resource's end and reads zero.
 
 constexpr int kRdWaves = 8;
-constexpr int kRdDepth = 2;
 
 struct RdPlan {
   int32_t tiles_m, tiles_n, splits, per;  // per: K-blocks per split
@@ -1231,6 +1283,225 @@ struct RdPlan {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rd_buffer(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
+
+// LDS bytes of the one-launch kernel: the staging slots, or the reduction
+// area that reuses them, whichever is larger.
+constexpr int rd_lds_bytes(int fm, int fn, int depth, int waves) {
+  const int stage = waves * depth * 16 * (fm + fn) * BK;
+  const int red = waves * fm * fn * 64 * 16;
+  return stage > red ? stage : red;
+}
+constexpr int kRdMaxLds = 128 * 1024;
+
+// The split hand-off of both one-launch kernels.  Wave `wave` holds the sums
+// of subtiles wave, wave + W, ... (OWN of them, those below SUB) for its
+// lanes.  Every workgroup of a split product stores them to its split's block
+// of the workspace and counts its arrival at the tile's counter; the last to
+// arrive replaces them with the sum over all splits, in split order, and
+// returns true (it stores the tile); the others return false.  The sums, the
+// counter and the final reads are device-scope atomic accesses, which the
+// hardware keeps coherent across the XCDs' separate L2 caches without writing
+// back or invalidating them (a device-scope fence would do both, for the
+// whole cache, in every workgroup).  The stores are complete (vmcnt 0)
+// before the workgroup's arrival counts.  The final reads are issued
+// kRdBatch splits at a time, all before the first is added.
+template <int SUB, int OWN, int W>
+__device__ __forceinline__ bool rd_split_sum(const RdPlan& q, int tile, int split, int wave, int lane, int64_t elems,
+                                             v4f (&sum)[OWN], int& last) {
+  constexpr int kRdBatch = 8;
+  const int64_t split_elems = (int64_t)q.tiles_m * q.tiles_n * elems;
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int t = wave + o * W;
+    if (t < SUB) {
+      float* mine = q.partials + split * split_elems + (((int64_t)tile * SUB + t) * 64 + lane) * 4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) __hip_atomic_store(mine + v, sum[o][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(q.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == q.splits - 1;
+  __syncthreads();
+  if (!last) return false;
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int t = wave + o * W;
+    if (t < SUB) {
+      sum[o] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      const float* src = q.partials + (((int64_t)tile * SUB + t) * 64 + lane) * 4;
+      for (int sp0 = 0; sp0 < q.splits; sp0 += kRdBatch) {
+        v4f part[kRdBatch];
+#pragma unroll
+        for (int b = 0; b < kRdBatch; ++b) {
+          part[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          if (sp0 + b < q.splits) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              part[b][v] = __hip_atomic_load(src + (sp0 + b) * split_elems + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kRdBatch; ++b)
+          if (sp0 + b < q.splits) sum[o] += part[b];
+      }
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(q.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+template <int FM, int FN, int DEPTH, int W, int VEC, bool POW2>
+__global__ __launch_bounds__(64 * W) void gemm_rd_kernel(GemmArgs p, RdPlan q) {
+  constexpr int TM = 16 * FM, TN = 16 * FN, ELEMS = TM * TN, SUB = FM * FN;
+  constexpr int ROWS = TM + TN, SLOT = ROWS * BK;
+  constexpr int OWN = (SUB + W - 1) / W;  // subtiles each wave finishes
+  static_assert(128 % TN == 0, "a tile's columns in one 128-column weight block");
+  static_assert(SUB <= W || SUB % W == 0, "subtiles shared evenly by the waves");
+  static_assert(rd_lds_bytes(FM, FN, DEPTH, W) <= kRdMaxLds, "LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[rd_lds_bytes(FM, FN, DEPTH, W)];
+  __shared__ int last;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int fr = lane & 15, fg = lane >> 4;
+  const int tiles = q.tiles_m * q.tiles_n;
+  const int tile = (int)(blockIdx.x % (unsigned)tiles), split = (int)(blockIdx.x / (unsigned)tiles);
+  const int tm = tile % q.tiles_m, tn = tile / q.tiles_m;
+  const uint32_t M = (uint32_t)p.M, N = (uint32_t)p.N, K = (uint32_t)p.K;
+  const uint32_t m0 = (uint32_t)tm * TM, n0 = (uint32_t)tn * TN;
+  const int kb_lo = split * q.per, kb_hi = kb_lo + q.per < q.nkb ? kb_lo + q.per : q.nkb;
+  const float* bsrow = p.b_s + (int64_t)(n0 / BK) * p.ldbs;
+
+  // the scales first (branch-free buffer loads: 0 for rows past M and
+  // K-blocks past the range), then the operands
+  float sa[DEPTH][FM], sb[DEPTH];
+  const auto rsa = rd_buffer(p.a_s, q.as_bytes);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int kb = kb_lo + wave + d * W;
+    const bool live = kb < kb_hi;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t m = m0 + 16 * i + fr;
+      sa[d][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rsa, (live && m < M) ? (m * (uint32_t)p.as_rs + (uint32_t)kb * (uint32_t)p.as_ks) * 4 : kOob, 0, 0));
+    }
+    sb[d] = live ? bsrow[kb] : 0.0f;
+  }
+  const i32x4 ra = make_rsrc(p.A, q.a_bytes), rb = make_rsrc(p.B, q.b_bytes);
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem));
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int kb = kb_lo + wave + d * W;
+    if (kb >= kb_hi) break;
+    const uint32_t slot = lds0 + (uint32_t)((wave * DEPTH + d) * SLOT), kbyte = (uint32_t)kb * BK;
+    if constexpr (VEC == 16) {
+      // instruction s: tile rows 8s .. 8s + 7 (all of A or all of B, TM being
+      // a multiple of 16); lane -> LDS chunk lane % 8 of row 8s + lane / 8
+#pragma unroll
+      for (int s = 0; s < ROWS / 8; ++s) {
+        const int r = 8 * s + (lane >> 3);
+        const uint32_t c = (uint32_t)((lane & 7) ^ swz_key(r)), kk = kbyte + 16 * c;
+        const bool isa = 8 * s < TM;
+        const uint32_t g = isa ? m0 + (uint32_t)r : n0 + (uint32_t)(r - TM);
+        const bool ok = (isa ? g < M : g < N) && kk < K;
+        dma_b128(isa ? ra : rb, slot + (uint32_t)(s * 1024), ok ? g * (uint32_t)(isa ? p.lda : p.ldb) + kk : kOob, 0);
+      }
+    } else {
+      static_assert(VEC == 8, "16- or 8-byte aligned rows");
+      // instruction s: tile rows 2s, 2s + 1; lane -> dword lane % 32 of row
+      // 2s + lane / 32 (K a multiple of 8: a dword is wholly before or past K)
+#pragma unroll
+      for (int s = 0; s < ROWS / 2; ++s) {
+        const int r = 2 * s + (lane >> 5), dw = lane & 31;
+        const uint32_t c = (uint32_t)((dw >> 2) ^ swz_key(r)), kk = kbyte + 16 * c + 4 * (uint32_t)(dw & 3);
+        const bool isa = 2 * s < TM;
+        const uint32_t g = isa ? m0 + (uint32_t)r : n0 + (uint32_t)(r - TM);
+        const bool ok = (isa ? g < M : g < N) && kk < K;
+        dma_b32(isa ? ra : rb, slot + (uint32_t)(s * 256), ok ? g * (uint32_t)(isa ? p.lda : p.ldb) + kk : kOob, 0);
+      }
+    }
+  }
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    if (kb_lo + wave + d * W >= kb_hi) break;
+    const uint8_t* sl = smem + (wave * DEPTH + d) * SLOT;
+    v8i bf[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[j] = read_frag(sl, TM + 16 * j + fr, fg);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const v8i af = read_frag(sl, 16 * i + fr, fg);
+      if constexpr (POW2) {
+        // a row past M carries scale 0 (2^-127) times a zero fragment
+        const int ea = (int)(__float_as_uint(sa[d][i]) >> 23), eb = (int)(__float_as_uint(sb[d]) >> 23);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, eb, 0, ea);
+      } else {
+        const float sc = sa[d][i] * sb[d];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                            0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc, acc[i][j][v]);
+        }
+      }
+    }
+  }
+  // Reduction area [wave][subtile][lane] over the staging slots: wait until
+  // every wave has read its fragments.
+  __syncthreads();
+  v4f* red = reinterpret_cast<v4f*>(smem);
+#pragma unroll
+  for (int t = 0; t < SUB; ++t) red[(wave * SUB + t) * 64 + lane] = acc[t / FN][t % FN];
+  __syncthreads();
+  // Wave w finishes subtiles w, w + W, ... (t = FN i + j): the waves'
+  // sums of its four outputs per lane (row 16i + fr, columns 16j + 4fg .. +3)
+  // added in wave order, each lane reading 16 consecutive bytes.
+  v4f sum[OWN];
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int t = wave + o * W;
+    sum[o] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (t < SUB) {
+      sum[o] = red[t * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < W; ++w) sum[o] += red[(w * SUB + t) * 64 + lane];
+    }
+  }
+  if (q.splits > 1 && !rd_split_sum<SUB, OWN, W>(q, tile, split, wave, lane, ELEMS, sum, last)) return;
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int t = wave + o * W;
+    if (t >= SUB) continue;
+    const uint32_t row = m0 + 16 * (t / FN) + fr, col = n0 + 16 * (t % FN) + 4 * fg;
+    if (row < M) {
+      uint16_t* dst = p.C + (int64_t)row * p.ldc + col;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (col + v < N) dst[v] = __builtin_bit_cast(uint16_t, (__bf16)sum[o][v]);
+    }
+  }
+}
+
+// Register-staged form of the one-launch kernel: each wave loads the MFMA
+// operands of up to kRdrDepth K-blocks straight into registers (16 rows of 64
+// bytes per instruction), so its LDS holds only the reduction area (64 KB at
+// 64x32 tiles) and two workgroups share a CU.  Used where the LDS-staged
+// form, at one workgroup per CU, would need more than one round of
+// workgroups or more K splits (64x4096x7168: 20.6 against 27.1 us;
+// 48x2048x7168 with ue8m0 scales: 13.2 against 16.4 us).
+constexpr int kRdrDepth = 2;
 
 // 32 bytes of one operand row for a lane (bytes k .. k + 31 of the row at
 // byte offset `row`, or kOob for a row to skip); VEC-byte pieces at or past K
@@ -1258,7 +1529,7 @@ __device__ __forceinline__ v8i rd_frag(__amdgpu_buffer_rsrc_t r, uint32_t row, u
 }
 
 template <int FM, int FN, int VEC, bool POW2>
-__global__ __launch_bounds__(64 * kRdWaves) void gemm_rd_kernel(GemmArgs p, RdPlan q) {
+__global__ __launch_bounds__(64 * kRdWaves) void gemm_rdr_kernel(GemmArgs p, RdPlan q) {
   constexpr int TM = 16 * FM, TN = 16 * FN, ELEMS = TM * TN;
   static_assert(FM * FN <= kRdWaves && 128 % TN == 0, "a wave per subtile; a tile's columns in one 128-block");
   __shared__ v4f red[kRdWaves][FM * FN][64];
@@ -1276,13 +1547,13 @@ __global__ __launch_bounds__(64 * kRdWaves) void gemm_rd_kernel(GemmArgs p, RdPl
   const auto rb = rd_buffer(p.B, q.b_bytes);
   const float* bsrow = p.b_s + (int64_t)(n0 / BK) * p.ldbs;
 
-  v8i bf[kRdDepth][FN], af[kRdDepth][FM];
-  float sa[kRdDepth][FM], sb[kRdDepth];
+  v8i bf[kRdrDepth][FN], af[kRdrDepth][FM];
+  float sa[kRdrDepth][FM], sb[kRdrDepth];
   // the scales first (branch-free buffer loads: 0 for rows past M and
   // K-blocks past the range), then the operands
   const auto rsa = rd_buffer(p.a_s, q.as_bytes);
 #pragma unroll
-  for (int d = 0; d < kRdDepth; ++d) {
+  for (int d = 0; d < kRdrDepth; ++d) {
     const int kb = kb_lo + wave + d * kRdWaves;
     const bool live = kb < kb_hi;
 #pragma unroll
@@ -1294,7 +1565,7 @@ __global__ __launch_bounds__(64 * kRdWaves) void gemm_rd_kernel(GemmArgs p, RdPl
     sb[d] = live ? bsrow[kb] : 0.0f;
   }
 #pragma unroll
-  for (int d = 0; d < kRdDepth; ++d) {
+  for (int d = 0; d < kRdrDepth; ++d) {
     const int kb = kb_lo + wave + d * kRdWaves;
     const bool live = kb < kb_hi;
     const uint32_t k = (uint32_t)kb * BK + 32 * fg;
@@ -1315,7 +1586,7 @@ __global__ __launch_bounds__(64 * kRdWaves) void gemm_rd_kernel(GemmArgs p, RdPl
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int d = 0; d < kRdDepth; ++d) {
+  for (int d = 0; d < kRdrDepth; ++d) {
     if (kb_lo + wave + d * kRdWaves >= kb_hi) break;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -1347,48 +1618,20 @@ __global__ __launch_bounds__(64 * kRdWaves) void gemm_rd_kernel(GemmArgs p, RdPl
   // order, each lane reading 16 consecutive bytes (no bank conflicts).
   const bool owner = wave < FM * FN;
   const int si = wave / FN, sj = wave % FN;
-  v4f sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f sum[1] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}};
   if (owner) {
-    sum = red[0][wave][lane];
+    sum[0] = red[0][wave][lane];
 #pragma unroll
-    for (int w = 1; w < kRdWaves; ++w) sum += red[w][wave][lane];
+    for (int w = 1; w < kRdWaves; ++w) sum[0] += red[w][wave][lane];
   }
-  if (q.splits > 1) {
-    // The sums, the counter and the final reads are device-scope atomic
-    // accesses, which the hardware keeps coherent across the XCDs' separate
-    // L2 caches without writing back or invalidating them (a device-scope
-    // fence would do both, for the whole cache, in every workgroup).  The
-    // stores are complete (vmcnt 0) before the workgroup's arrival counts.
-    const int64_t slot = ((int64_t)tile * FM * FN + wave) * 64 + lane;   // within one split's block
-    const int64_t split_elems = (int64_t)tiles * ELEMS;
-    if (owner) {
-      float* mine = q.partials + split * split_elems + slot * 4;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) __hip_atomic_store(mine + v, sum[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(q.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == q.splits - 1;
-    __syncthreads();
-    if (!last) return;
-    if (owner) {
-      sum = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int sp = 0; sp < q.splits; ++sp) {
-        const float* src = q.partials + sp * split_elems + slot * 4;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sum[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(q.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (q.splits > 1 && !rd_split_sum<FM * FN, 1, kRdWaves>(q, tile, split, wave, lane, ELEMS, sum, last)) return;
   if (!owner) return;
   const uint32_t row = m0 + 16 * si + fr, col = n0 + 16 * sj + 4 * fg;
   if (row < M) {
     uint16_t* dst = p.C + (int64_t)row * p.ldc + col;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (col + v < N) dst[v] = __builtin_bit_cast(uint16_t, (__bf16)sum[v]);
+      if (col + v < N) dst[v] = __builtin_bit_cast(uint16_t, (__bf16)sum[0][v]);
   }
 }
 
@@ -1695,14 +1938,21 @@ int gemm_k_splits(int64_t M, int64_t N, int64_t K) {
   return (int)((nkb + per - 1) / per);     // no empty split
 }
 
-// Tile shape and K split of the one-launch small-product kernel: 32-row tiles
-// for at most 32 rows, else 64; 64 columns (32 when that leaves fewer than
-// 256 workgroups); one K-block per wave when one workgroup covers K, else two
-// per wave (fewer splits: decode 32x1536x7168 9.9 against 11.2 us, 64x4096x7168
-// 20.4 against 25.1 us; three or four per wave were slower on the decode
-// shape).
+// Tile shape, K split and form of the one-launch small-product kernel.
+// 32-row tiles for at most 32 rows, else 64.  The LDS-staged form takes the
+// first of these that fits in one round of workgroups (one per CU) with at
+// most 4 K splits: for 32-row tiles 64 then 32 columns, for 64-row tiles 32
+// then 64 columns; each wave takes one K-block, or two where their staging
+// fits in LDS and the range needs more than one workgroup (fewer splits:
+// decode 32x1536x7168 9.9 against 11.2 us).  Otherwise the register-staged
+// form: 64 columns for 32-row tiles unless that leaves fewer than 256
+// workgroups, else 32, two K-blocks per wave when K is split.  Measured
+// (graph of launches, weights rotated): decode 32x1536x7168 8.8 us
+// (register-staged 10.0), ragged 333x2500x1000 with 64x64 tiles 9.0 us
+// (64x32 tiles: 11.5; register-staged 10.2), 100x1024x4096 10.5 us (12.2).
 struct RdShape {
-  int fm, fn;
+  int fm, fn, depth;
+  bool regs;  // register-staged form
   int64_t tiles_m, tiles_n, splits, per, nkb;
 };
 
@@ -1710,19 +1960,28 @@ RdShape rd_shape(int64_t M, int64_t N, int64_t K) {
   RdShape r{};
   r.nkb = (K + BK - 1) / BK;
   r.fm = M <= 32 ? 2 : 4;
-  auto make = [&](int fn) {
+  // one round of workgroups at one per CU on a 256-CU part (a constant, so
+  // that the workspace size does not depend on the device)
+  constexpr int64_t kRound = 256;
+  auto make = [&](int fn, bool regs) {
     r.fn = fn;
+    r.regs = regs;
+    r.depth = 1;
     r.tiles_m = (M + 16 * r.fm - 1) / (16 * r.fm);
     r.tiles_n = (N + 16 * fn - 1) / (16 * fn);
     r.per = kRdWaves;
     r.splits = (r.nkb + r.per - 1) / r.per;
-    if (r.splits > 1) {
-      r.per = kRdWaves * kRdDepth;
+    if (r.splits > 1 && (regs || rd_lds_bytes(r.fm, fn, 2, kRdWaves) <= kRdMaxLds)) {
+      r.depth = 2;
+      r.per = 2 * kRdWaves;
       r.splits = (r.nkb + r.per - 1) / r.per;
     }
+    return r.tiles_m * r.tiles_n * r.splits;
   };
-  make(r.fm == 4 ? 2 : 4);
-  if (r.fm == 2 && r.tiles_m * r.tiles_n * r.splits < 256) make(2);
+  const int first = r.fm == 2 ? 4 : 2, second = 6 - first;
+  for (int fn : {first, second})
+    if (make(fn, false) <= kRound && r.splits <= 4) return r;
+  if (make(r.fm == 4 ? 2 : 4, true) < kRound && r.fm == 2) make(2, true);
   return r;
 }
 
@@ -1755,15 +2014,29 @@ int rd_vec(const GemmArgs& a) {
   return 0;
 }
 
-template <int FM, int FN>
+template <int FM, int FN, int DEPTH>
 hipError_t launch_rd(const GemmArgs& a, const RdPlan& q, int vec, dim3 grid, hipStream_t stream) {
+  constexpr int W = kRdWaves;
+  const dim3 blk(64 * W);
+  if (vec == 16) {
+    if (a.pow2) hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, DEPTH, W, 16, true>), grid, blk, 0, stream, a, q);
+    else hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, DEPTH, W, 16, false>), grid, blk, 0, stream, a, q);
+  } else {
+    if (a.pow2) hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, DEPTH, W, 8, true>), grid, blk, 0, stream, a, q);
+    else hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, DEPTH, W, 8, false>), grid, blk, 0, stream, a, q);
+  }
+  return hipGetLastError();
+}
+
+template <int FM, int FN>
+hipError_t launch_rdr(const GemmArgs& a, const RdPlan& q, int vec, dim3 grid, hipStream_t stream) {
   const dim3 blk(64 * kRdWaves);
   if (vec == 16) {
-    if (a.pow2) hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 16, true>), grid, blk, 0, stream, a, q);
-    else hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 16, false>), grid, blk, 0, stream, a, q);
+    if (a.pow2) hipLaunchKernelGGL((gemm_rdr_kernel<FM, FN, 16, true>), grid, blk, 0, stream, a, q);
+    else hipLaunchKernelGGL((gemm_rdr_kernel<FM, FN, 16, false>), grid, blk, 0, stream, a, q);
   } else {
-    if (a.pow2) hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 8, true>), grid, blk, 0, stream, a, q);
-    else hipLaunchKernelGGL((gemm_rd_kernel<FM, FN, 8, false>), grid, blk, 0, stream, a, q);
+    if (a.pow2) hipLaunchKernelGGL((gemm_rdr_kernel<FM, FN, 8, true>), grid, blk, 0, stream, a, q);
+    else hipLaunchKernelGGL((gemm_rdr_kernel<FM, FN, 8, false>), grid, blk, 0, stream, a, q);
   }
   return hipGetLastError();
 }
@@ -1775,7 +2048,9 @@ hipError_t launch_rd(const GemmArgs& a, const RdPlan& q, int vec, dim3 grid, hip
 // (32 x 36864 x 7168: 112 vs 65 us).
 bool skinny_ok(const GemmArgs& a) {
   const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && a.N > kSkinny32MinN && a.N <= kSkinny32MaxN);
-  return rows && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16);
+  // a workgroup's 16 weight rows under one descriptor with 32-bit offsets
+  const bool span = 15 * a.ldb + a.K < ((int64_t)1 << 31);
+  return rows && span && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16);
 }
 
 // Split K over workgroups for operands the one-launch kernel does not take:
@@ -1838,9 +2113,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
       q.counters = reinterpret_cast<int32_t*>(ws);
       q.partials = reinterpret_cast<float*>(ws + cbytes);
       const dim3 grid((unsigned)(r.tiles_m * r.tiles_n * r.splits));
-      if (r.fm == 2 && r.fn == 4) return launch_rd<2, 4>(a, q, vec, grid, stream);
-      if (r.fm == 2) return launch_rd<2, 2>(a, q, vec, grid, stream);
-      return launch_rd<4, 2>(a, q, vec, grid, stream);
+      if (r.regs) {
+        if (r.fm == 2 && r.fn == 4) return launch_rdr<2, 4>(a, q, vec, grid, stream);
+        if (r.fm == 2) return launch_rdr<2, 2>(a, q, vec, grid, stream);
+        return launch_rdr<4, 2>(a, q, vec, grid, stream);
+      }
+      if (r.fm == 2 && r.fn == 4) return launch_rd<2, 4, 1>(a, q, vec, grid, stream);
+      if (r.fm == 2) return r.depth == 2 ? launch_rd<2, 2, 2>(a, q, vec, grid, stream)
+                                         : launch_rd<2, 2, 1>(a, q, vec, grid, stream);
+      if (r.fn == 4) return launch_rd<4, 4, 1>(a, q, vec, grid, stream);
+      return launch_rd<4, 2, 1>(a, q, vec, grid, stream);
     }
     GemmArgs b = a;
     b.partial = reinterpret_cast<float*>(ws + cbytes);

@@ -205,6 +205,30 @@ def test_decode_rows(M, N, K, fmt):
         check_gemm_full(run(a, a_s, b, b_s, layout, scale_fmt=fmt), a, a_s, b, b_s, f"{M}x{N}x{K} {fmt} {layout}")
 
 
+@pytest.mark.parametrize("M,N,K,fmt", [
+    (32, 1024, 1024, "fp32"),     # staged in LDS, 32x64 tiles, one workgroup per tile
+    (32, 1024, 4096, "ue8m0"),    # the same, K split 4 ways
+    (20, 1000, 1000, "fp32"),     # 32x64 tiles, rows only 8-byte aligned (4-byte loads to LDS)
+    (30, 1000, 3000, "ue8m0"),    # the same, K split 3 ways
+    (24, 2048, 7168, "fp32"),     # 32x32 tiles, two K-blocks per wave, K split 4 ways
+    (32, 600, 7000, "fp32"),      # the same with 8-byte aligned rows
+    (100, 1000, 4096, "fp32"),    # 64x32 tiles, K split 4 ways
+    (70, 900, 2008, "ue8m0"),     # the same with 8-byte aligned rows, K split 2 ways
+    (333, 2500, 1000, "fp32"),    # 64x64 tiles, 8-byte aligned rows
+    (64, 4096, 7168, "fp32"),     # operands staged in registers, 64x32 tiles
+    (48, 2048, 7000, "ue8m0"),    # the same with 8-byte aligned rows
+    (32, 2048, 16384, "fp32"),    # registers, 32x64 tiles, K split 8 ways
+    (32, 1024, 16384, "ue8m0"),   # registers, 32x32 tiles
+])
+def test_one_launch_forms(M, N, K, fmt):
+    """Products with few output tiles run in one launch of the small-product
+    kernel, in the form and tile shape their size selects (comments above:
+    where the operands are staged, the tile, the load width for rows that are
+    only 8-byte aligned, the K split): each against the oracle in full."""
+    a, a_s, b, b_s = operands(M, N, K, I.DECODE_QA, ue8m0=(fmt == "ue8m0"), outliers=0.01)
+    check_gemm_full(run(a, a_s, b, b_s, "kb", scale_fmt=fmt), a, a_s, b, b_s, f"{M}x{N}x{K} {fmt}")
+
+
 def test_dense_ffn_up_sampled():
     _sampled_product(4096, 18432, 7168, 50, 256, 4)
 
