@@ -215,8 +215,20 @@ __global__ __launch_bounds__(kThreads) void act_quant_lean_kernel(ActQuantArgs a
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const uint32_t w = base + i * waves;
-      const uint32_t b = fastdiv(w, G);
-      const uint32_t m = (w - b * G.d) * 4 + drow;
+      // Unit w: 4 rows of one K-block.  Units go row group by row group (G
+      // divides by the K-block count), so a workgroup's 4 waves read 1 KB of
+      // each of 4 rows; the gathered form goes block by block (G divides by
+      // the row-group count), where neighbouring waves often read the same
+      // source rows.
+      uint32_t b, m;
+      if constexpr (ROWS) {
+        b = fastdiv(w, G);
+        m = (w - b * G.d) * 4 + drow;
+      } else {
+        const uint32_t g = fastdiv(w, G);
+        b = w - g * G.d;
+        m = g * 4 + drow;
+      }
       const uint32_t col = b * kBlock + lane16 * 8;
       const bool live = w < e.total && m < M;
       const bool in = live && col < K;
@@ -494,9 +506,16 @@ hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
   if (vec && fast && ex < lim && eu < lim && ey < lim && eh < lim && es < lim && er < lim && units < lim) {
     LeanExtents e{(uint32_t)nb, (uint32_t)units, (uint32_t)ex, (uint32_t)eu, (uint32_t)ey,
                   (uint32_t)es, (uint32_t)eh, (uint32_t)er};
-    if (fused) hipLaunchKernelGGL((act_quant_lean_kernel<true, false>), g, blk, 0, stream, a, gdiv, e);
+    // Row-group order against block order (measured, graph of launches):
+    // [4096, 7168] 16.9 against 17.3 us, [4096, 18432] 39.5 against 44.4 us,
+    // [32768, 7168] 117.9 against 120.2 us, the fused gate on [4096, 18432]
+    // 71.1 against 77.3 us; the gathered rows 106.2 against 97.5 us, so they
+    // keep the block order.  (One row and four K-blocks per wave, in either
+    // order, was slower than both: 18.6 us on [4096, 7168].)
+    const FastDiv nbdiv = make_fastdiv((uint32_t)nb);
+    if (fused) hipLaunchKernelGGL((act_quant_lean_kernel<true, false>), g, blk, 0, stream, a, nbdiv, e);
     else if (a.rows != nullptr) hipLaunchKernelGGL((act_quant_lean_kernel<false, true>), g, blk, 0, stream, a, gdiv, e);
-    else hipLaunchKernelGGL((act_quant_lean_kernel<false, false>), g, blk, 0, stream, a, gdiv, e);
+    else hipLaunchKernelGGL((act_quant_lean_kernel<false, false>), g, blk, 0, stream, a, nbdiv, e);
     return hipGetLastError();
   }
   if (fused) {
