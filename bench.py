@@ -529,6 +529,57 @@ def bench_small_gemm(dev, iters, name, M, N, K, fmt, outlier):
             "weight_copies_rotated": copies, "timing": "HIP graph of back-to-back launches"}
 
 
+def bench_grouped_classes(dev, reps):
+    """The routed-expert products (dim 7168, inter 2048, fp32 scales) with
+    uniform expert sizes that each fill one tile class of the grouped kernel:
+    256 experts of 41 rows (64-row tiles), 256 of 100 rows (128-row tiles)
+    and 32 of 1024 rows (256-row tiles).  Per launch: time, FP8 rate and the
+    rate at which the experts' weights stream; for per-class counters."""
+    d = I.WORKLOADS["moe"].dims
+    D, F = d["dim"], d["inter"]
+    cfgs = [("64-row tiles: 256 experts x 41 rows", 256, 41), ("128-row tiles: 256 experts x 100 rows", 256, 100),
+            ("256-row tiles: 32 experts x 1024 rows", 32, 1024)]
+    EM = max(E for _, E, _ in cfgs)
+    q13 = torch.empty((EM, 2 * F, D), dtype=torch.uint8, device=dev)
+    s13 = torch.empty((EM, kb(2 * F), kb(D)), dtype=torch.float32, device=dev)
+    q2 = torch.empty((EM, D, F), dtype=torch.uint8, device=dev)
+    s2 = torch.empty((EM, kb(D), kb(F)), dtype=torch.float32, device=dev)
+    for e in range(EM):
+        q, s = ds.weight_quant(I.device_normal((2 * F, D), seed=10_000 + e, std=0.02, device=dev))
+        q13[e].copy_(q)
+        s13[e].copy_(s)
+        q, s = ds.weight_quant(I.device_normal((D, F), seed=20_000 + e, std=0.02, device=dev))
+        q2[e].copy_(q)
+        s2[e].copy_(s)
+    del q, s
+    res = {}
+    for name, E, r in cfgs:
+        M = E * r
+        xq, xs = ds.act_quant(I.device_normal((M, D), seed=401, std=1.0, device=dev, dtype=torch.bfloat16))
+        offd = (torch.arange(E + 1, dtype=torch.int32, device=dev) * r).contiguous()
+        hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
+        hs = ds.new_scales(M, kb(F), dev)
+        yr = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+        lib = ds._lib.load()
+        ws = torch.empty(lib.dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
+        T = Timer()
+        a13, a2 = q13[:E], q2[:E]
+        for it in range(reps + 1):
+            T.run("up", lambda: ds.grouped_gemm_silu_mul_act_quant(xq, xs, a13, s13[:E], offd, out=(hq, hs),
+                                                                   workspace=ws))
+            T.run("down", lambda: ds.grouped_gemm(hq, hs, a2, s2[:E], offd, out=yr, workspace=ws))
+            T.collect()
+            if it == 0:
+                T.reset()
+        out = {}
+        for k, fl, wb in (("up", 2.0 * M * 2 * F * D, E * 2 * F * D), ("down", 2.0 * M * D * F, E * D * F)):
+            us = T.avg_us(k)
+            out[k] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "weight_gbs": round(wb / us / 1e3, 1)}
+        res[name] = out
+        del xq, xs, hq, hs, yr, ws
+    return res
+
+
 # ---- CPU baseline ---------------------------------------------------------------------------
 
 def cpu_baseline(budget_s=15.0):
@@ -613,6 +664,9 @@ def only(kernel, reps, dev, fmt="fp32"):
     if kernel == "routed_experts":
         print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps)}))
         return
+    if kernel == "grouped_classes":
+        print(json.dumps({"only": kernel, "reps": reps, "result": bench_grouped_classes(dev, reps)}))
+        return
     if kernel == "small_products":
         res = {"decode_qa": bench_small_gemm(dev, reps, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True),
                "ragged_ue8m0": bench_small_gemm(dev, reps, "ragged ue8m0: 333x2500x1000", 333, 2500, 1000, "ue8m0",
@@ -659,7 +713,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["act_quant", "weight_dequant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
-                                       "copy", "routed_experts", "small_products"],
+                                       "copy", "routed_experts", "small_products", "grouped_classes"],
                     help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
                          "(for rocprofv3)")
     ap.add_argument("--reps", type=int, default=3)

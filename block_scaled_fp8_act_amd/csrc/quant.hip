@@ -208,12 +208,15 @@ __global__ __launch_bounds__(kThreads) void act_quant_lean_kernel(ActQuantArgs a
   const uint32_t ldg = (uint32_t)a.ldg, ldu = (uint32_t)a.ldu, ldy = (uint32_t)a.ldy, ldh = (uint32_t)a.ldh;
   const uint32_t srs = (uint32_t)a.s_rs, sks = (uint32_t)a.s_ks;
   const bool want_h = FUSED && a.h != nullptr;
-  for (uint32_t base = wave0; base < e.total; base += waves * kUnroll) {
-    u32x4 wg[kUnroll], wu[kUnroll];
-    uint32_t ms[kUnroll], cs[kUnroll], bs[kUnroll];
-    bool lv[kUnroll];
+  // Units in flight per wave: one for the fused form (70.9 -> 67.4 us on the
+  // gate of [4096, 18432]; the plain and gathered forms are faster with two).
+  constexpr int U = FUSED ? 1 : kUnroll;
+  for (uint32_t base = wave0; base < e.total; base += waves * U) {
+    u32x4 wg[U], wu[U];
+    uint32_t ms[U], cs[U], bs[U];
+    bool lv[U];
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < U; ++i) {
       const uint32_t w = base + i * waves;
       // Unit w: 4 rows of one K-block.  Units go row group by row group (G
       // divides by the K-block count), so a workgroup's 4 waves read 1 KB of
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_lean_kernel(ActQuantArgs a
       if (FUSED) wu[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, in ? (m * ldu + col) * 2 : kOffNone, 0, kNt);
     }
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < U; ++i) {
       const bool in = lv[i] && cs[i] < K;
       float v[8];
       unpack8(wg[i], v);
