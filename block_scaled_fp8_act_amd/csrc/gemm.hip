@@ -1091,7 +1091,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 // Products with at most 16 rows (decode at small batch): the weight is
 // streamed once and every output needs all of K, so one workgroup of
 // kSkinnyWaves waves owns 16 output columns over the whole of K.  Its waves
-// take the K-blocks in turn (wave w: w, w + W, ...), kSkinnyDepth K-blocks in
+// take the K-blocks in turn (wave w: w, w + W, ...), skinny_depth K-blocks in
 // flight: the weight's 16 rows of each K-block go straight to the wave's own
 // LDS slot as two 8-row, full-line segments (the large kernels' swizzled
 // layout), the activation fragments straight into registers; the wave then
@@ -1100,21 +1100,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 // staging slots again) and rounded to bf16.  No split of K across
 // workgroups, so no fp32 partials and no second kernel.  Against loading the
 // weight fragment into registers (16 rows of 64 bytes per instruction, half
-// of each line): 1x7168x18432 26.5 against 28.9 us, 4x36864x7168 54.2
-// against 57.9, 8x1536x7168 7.0 against 8.3, 32x4096x7168 12.8 against
-// 13.6; 1x18432x7168 unchanged (29.4 us; 32.9 against 31.9 with ue8m0
-// scales).  Nontemporal loads of the weight measured 8% slower; a fourth
-// K-block per wave was no faster at one row and slower at 32.
+// of each line), at three K-blocks per wave: 1x7168x18432 26.5 against 28.9
+// us, 4x36864x7168 54.2 against 57.9, 8x1536x7168 7.0 against 8.3.  Fewer
+// K-blocks per wave then let two workgroups share a CU (64 KB of LDS or less
+// and at most 92 registers, against 123 at three): one K-block per wave
+// 1x18432x7168 29.5 -> 24.1 us, 4x36864x7168 54.1 -> 43.9, 32x7168x2048
+// 10.0 -> 8.0, 8x1536x7168 7.0 -> 6.5; with ue8m0 scales and one activation
+// fragment two K-blocks per wave are faster still (1x18432x7168 25.6 against
+// 27.9 us at one, 33.0 at three; 4x36864x7168 46.6 against 49.3).  8 or 12
+// waves per workgroup were no better; nontemporal loads of the weight
+// measured 8% slower.
 constexpr int kSkinnyWaves = 16;
-constexpr int kSkinnyDepth = 3;
+constexpr int skinny_depth(bool pow2, int frags) { return pow2 && frags == 1 ? 2 : 1; }
 constexpr int kSkinnyRows = 16;
-// 17 to 32 rows take the two-fragment form for 2048 < N <= 8192 only
-// (measured against split K: 32x7168x2048 10.9 vs 13.7 us, 32x4096x7168 14.0
-// vs 14.6 us; with N <= 2048 there are too few workgroups to stream the
-// weight (32x1536x7168: 13.4 vs 12.5 us), and beyond 8192 every 16-column
-// workgroup's re-read of all rows of A outweighs the saving (32x18432x7168:
-// 60 vs 55 us)).
-constexpr int64_t kSkinny32MinN = 2048, kSkinny32MaxN = 8192;
+// 17 to 32 rows take the two-fragment form where it measured faster than the
+// one-launch small-product kernel and the tiled kernels:
+// * 2048 < N <= 8192 (32x7168x2048 8.0 against 9.6 us, 32x4096x7168 12.9
+//   against 13.7, 17x2100x1040 with ue8m0 scales 3.5 against 7.1);
+// * N and K at most 2048: every wave takes one K-block, one pass, no split
+//   (17x1000x1040 3.3 against 6.9 us, 32x2048x2048 5.6 against 8.0,
+//   32x256x2048 4.9 against 6.9);
+// * 16384 <= N < 32768 with K > 2048, where the tiled kernel has fewer
+//   64x128 tiles than CUs (32x18432x7168 46.3 against 54.9 us, 24x16384x4096
+//   20.9 against 32.3; with K = 2048 the tiled kernel stays faster,
+//   32x30000x2048 19.0 against 23.4).
+// Not below N = 2048 with longer K (32x1536x7168 12.3 against 9.0 us: too few
+// workgroups to stream the weight) nor from N = 32768 (32x36864x7168 83
+// against 63 us: every 16-column workgroup re-reads all activation rows).
+inline bool skinny_two_fragment(int64_t N, int64_t K) {
+  return (N > 2048 && N <= 8192) || (N <= 2048 && K <= 2048) || (N >= 16384 && N < 32768 && K > 2048);
+}
 
 // 32 bytes of one operand row for a lane: two 16-byte chunks; a chunk at or
 // past K (K is a multiple of 16 here) or of a row outside the matrix reads as
@@ -1132,10 +1147,11 @@ __device__ __forceinline__ v8i skinny_frag(const uint8_t* row, bool valid, int64
 // FRAGS 16-row activation fragments (up to 16 * FRAGS rows): each wave
 // multiplies its weight fragment by every activation fragment of a K-block.
 constexpr int kSkinnySlot = 16 * BK;  // one K-block of the 16 weight rows
-constexpr int kSkinnyLds = kSkinnyWaves * kSkinnyDepth * kSkinnySlot;
 
 template <bool POW2, int FRAGS>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs p) {
+  constexpr int kSkinnyDepth = skinny_depth(POW2, FRAGS);
+  constexpr int kSkinnyLds = kSkinnyWaves * kSkinnyDepth * kSkinnySlot;
   static_assert(kSkinnyLds >= kSkinnyWaves * FRAGS * 64 * 16, "reduction area within the staging slots");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSkinnyLds];
   float (*red)[FRAGS][64][4] = reinterpret_cast<float (*)[FRAGS][64][4]>(smem);
@@ -2042,12 +2058,11 @@ hipError_t launch_rdr(const GemmArgs& a, const RdPlan& q, int vec, dim3 grid, hi
 }
 
 // The skinny kernel loads 16-byte chunks of A and B rows.  Measured against
-// the tiled kernels it is faster up to 16 rows (1 x 18432 x 7168: 29 vs 52 us;
-// 16 x 7168 x 2048: 8.0 vs 12.1 us) and not beyond: at 32 rows every
-// 16-column workgroup re-reads twice the weight's bytes of activations
-// (32 x 36864 x 7168: 112 vs 65 us).
+// the tiled kernels it is faster up to 16 rows (1 x 18432 x 7168: 24 vs 52 us;
+// 16 x 7168 x 2048: 6.0 vs 12.1 us); from 17 to 32 rows see
+// skinny_two_fragment.
 bool skinny_ok(const GemmArgs& a) {
-  const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && a.N > kSkinny32MinN && a.N <= kSkinny32MaxN);
+  const bool rows = a.M <= kSkinnyRows || (a.M <= 2 * kSkinnyRows && skinny_two_fragment(a.N, a.K));
   // a workgroup's 16 weight rows under one descriptor with 32-bit offsets
   const bool span = 15 * a.ldb + a.K < ((int64_t)1 << 31);
   return rows && span && a.K % 16 == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 && aligned(a.A, 16) && aligned(a.B, 16);

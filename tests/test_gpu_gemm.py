@@ -195,11 +195,13 @@ def _sampled_product(M, N, K, seed, row_pick, nblocks, fmt="fp32"):
 
 @pytest.mark.parametrize("M,N,K,fmt", [(1, 4608, 7168, "fp32"), (16, 7168, 2048, "fp32"), (8, 1536, 7168, "ue8m0"),
                                        (5, 300, 1040, "fp32"), (16, 129, 16, "ue8m0"),
-                                       (32, 7168, 2048, "fp32"), (17, 2100, 1040, "ue8m0"), (24, 4100, 528, "fp32")])
+                                       (32, 7168, 2048, "fp32"), (17, 2100, 1040, "ue8m0"), (24, 4100, 528, "fp32"),
+                                       (17, 1000, 1040, "fp32"), (32, 256, 2048, "ue8m0"), (24, 16384, 4096, "fp32")])
 def test_decode_rows(M, N, K, fmt):
-    # at most 16 rows with K % 16 == 0 (and 17 to 32 rows for 2048 < N <= 8192,
-    # two activation fragments): the kernel that splits K across the waves of
-    # one workgroup per 16 columns (ragged N and K included)
+    # at most 16 rows with K % 16 == 0 (and 17 to 32 rows with two activation
+    # fragments for 2048 < N <= 8192, for N and K at most 2048, and for
+    # 16384 <= N < 32768 with K > 2048): the kernel that splits K across the
+    # waves of one workgroup per 16 columns (ragged N and K included)
     a, a_s, b, b_s = operands(M, N, K, I.DECODE_QA, ue8m0=(fmt == "ue8m0"), outliers=0.01)
     for layout in ("kb", "row"):
         check_gemm_full(run(a, a_s, b, b_s, layout, scale_fmt=fmt), a, a_s, b, b_s, f"{M}x{N}x{K} {fmt} {layout}")
