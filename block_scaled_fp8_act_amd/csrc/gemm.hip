@@ -20,8 +20,11 @@
 //
 // Kernels: gemm_persistent_kernel (one workgroup per CU walking its XCD's
 // 256x256 tiles) for large dense products, plain or with the SiLU gate and
-// act_quant in the epilogue; gemm_kernel (one workgroup per tile, split K
-// through a workspace when there are few tiles) otherwise;
+// act_quant in the epilogue; gemm_kernel (one workgroup per tile) otherwise;
+// for products with few output tiles gemm_rd_kernel and gemm_rdr_kernel (one
+// launch: K split over the waves of a workgroup and, through arrival
+// counters in the workspace, over workgroups), or gemm_kernel with split K
+// and splitk_reduce_kernel for operands those do not take;
 // skinny_gemm_kernel for decode rows; grouped_merged_kernel for the
 // per-expert products (three tile heights in one launch, scheduled by
 // tile_schedule_kernel from the device-side offsets).
