@@ -11,6 +11,8 @@
 // and two fma.  Work is distributed as (row, block) units in a grid-stride
 // loop sized to the machine; each lane keeps kUnroll independent 16-byte loads
 // in flight.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -190,14 +192,14 @@ struct LeanExtents {
   uint32_t x, u, y, s, h, rows;          // resource sizes in bytes
 };
 
-template <bool FUSED, bool ROWS>
-__global__ __launch_bounds__(kThreads) void act_quant_lean_kernel(ActQuantArgs a, FastDiv G, LeanExtents e) {
+template <bool FUSED, bool ROWS, int THREADS>
+__global__ __launch_bounds__(THREADS) void act_quant_lean_kernel(ActQuantArgs a, FastDiv G, LeanExtents e) {
   constexpr int kNt = 2;  // cache-policy bit of a nontemporal access
   const int lane = threadIdx.x & 63;
   const uint32_t lane16 = lane & 15;
   const uint32_t drow = lane >> 4;
-  const uint32_t waves = gridDim.x * (kThreads / 64);
-  const uint32_t wave0 = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t waves = gridDim.x * (THREADS / 64);
+  const uint32_t wave0 = blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6);
   const auto rx = buffer_of(a.g, e.x);
   const auto ru = buffer_of(FUSED ? static_cast<const void*>(a.u) : static_cast<const void*>(a.g), e.u);
   const auto ry = buffer_of(a.y, e.y);
@@ -516,10 +518,26 @@ hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
     // keep the block order.  (One row and four K-blocks per wave, in either
     // order, was slower than both: 18.6 us on [4096, 7168].)
     const FastDiv nbdiv = make_fastdiv((uint32_t)nb);
-    if (fused) hipLaunchKernelGGL((act_quant_lean_kernel<true, false>), g, blk, 0, stream, a, nbdiv, e);
-    else if (a.rows != nullptr) hipLaunchKernelGGL((act_quant_lean_kernel<false, true>), g, blk, 0, stream, a, gdiv, e);
-    else hipLaunchKernelGGL((act_quant_lean_kernel<false, false>), g, blk, 0, stream, a, nbdiv, e);
-    return hipGetLastError();
+    // Workgroups of 2 waves, or of 1 wave for the plain form when the grid
+    // covers every unit in one pass (the same 32 x 4 waves per CU at most):
+    // against 4 waves, [4096, 7168] 16.2 us with 1 wave and 16.9 with 2
+    // against 17.1; [32768, 7168] 116.7 us with 2 waves, 121.7 with 1,
+    // 118.5 with 4; 8 or 16 waves were slower on every shape.
+    auto lean = [&](auto threads_c) {
+      constexpr int W = decltype(threads_c)::value / 64;
+      const int64_t want_w = (units + W * kUnroll - 1) / (W * kUnroll);
+      const int64_t cap_w = (int64_t)device_cu_count() * (fused ? 8 : 32) * (kThreads / 64) / W;
+      const dim3 gw((unsigned)(want_w < cap_w ? want_w : cap_w)), bw(64 * W);
+      if (fused) hipLaunchKernelGGL((act_quant_lean_kernel<true, false, 64 * W>), gw, bw, 0, stream, a, nbdiv, e);
+      else if (a.rows != nullptr)
+        hipLaunchKernelGGL((act_quant_lean_kernel<false, true, 64 * W>), gw, bw, 0, stream, a, gdiv, e);
+      else hipLaunchKernelGGL((act_quant_lean_kernel<false, false, 64 * W>), gw, bw, 0, stream, a, nbdiv, e);
+      return hipGetLastError();
+    };
+    const int64_t one_pass = (units + kUnroll - 1) / kUnroll;  // 1-wave workgroups wanted
+    if (!fused && a.rows == nullptr && one_pass <= (int64_t)device_cu_count() * 32 * (kThreads / 64))
+      return lean(std::integral_constant<int, 64>());
+    return lean(std::integral_constant<int, 128>());
   }
   if (fused) {
     if (vec) hipLaunchKernelGGL((act_quant_kernel<true, true>), g, blk, 0, stream, a, nb, gdiv, fast);
