@@ -192,7 +192,7 @@ struct LeanExtents {
   uint32_t x, u, y, s, h, rows;          // resource sizes in bytes
 };
 
-template <bool FUSED, bool ROWS, int THREADS>
+template <bool FUSED, bool ROWS, int THREADS, int U>
 __global__ __launch_bounds__(THREADS) void act_quant_lean_kernel(ActQuantArgs a, FastDiv G, LeanExtents e) {
   constexpr int kNt = 2;  // cache-policy bit of a nontemporal access
   const int lane = threadIdx.x & 63;
@@ -210,9 +210,6 @@ __global__ __launch_bounds__(THREADS) void act_quant_lean_kernel(ActQuantArgs a,
   const uint32_t ldg = (uint32_t)a.ldg, ldu = (uint32_t)a.ldu, ldy = (uint32_t)a.ldy, ldh = (uint32_t)a.ldh;
   const uint32_t srs = (uint32_t)a.s_rs, sks = (uint32_t)a.s_ks;
   const bool want_h = FUSED && a.h != nullptr;
-  // Units in flight per wave: one for the fused form (70.9 -> 67.4 us on the
-  // gate of [4096, 18432]; the plain and gathered forms are faster with two).
-  constexpr int U = FUSED ? 1 : kUnroll;
   for (uint32_t base = wave0; base < e.total; base += waves * U) {
     u32x4 wg[U], wu[U];
     uint32_t ms[U], cs[U], bs[U];
@@ -518,26 +515,35 @@ hipError_t launch_act_quant(const ActQuantArgs& a, hipStream_t stream) {
     // keep the block order.  (One row and four K-blocks per wave, in either
     // order, was slower than both: 18.6 us on [4096, 7168].)
     const FastDiv nbdiv = make_fastdiv((uint32_t)nb);
-    // Workgroups of 2 waves, or of 1 wave for the plain form when the grid
-    // covers every unit in one pass (the same 32 x 4 waves per CU at most):
-    // against 4 waves, [4096, 7168] 16.2 us with 1 wave and 16.9 with 2
-    // against 17.1; [32768, 7168] 116.7 us with 2 waves, 121.7 with 1,
-    // 118.5 with 4; 8 or 16 waves were slower on every shape.
-    auto lean = [&](auto threads_c) {
-      constexpr int W = decltype(threads_c)::value / 64;
-      const int64_t want_w = (units + W * kUnroll - 1) / (W * kUnroll);
-      const int64_t cap_w = (int64_t)device_cu_count() * (fused ? 8 : 32) * (kThreads / 64) / W;
+    // Waves per workgroup (W), units in flight per wave (U) and the most
+    // waves in the grid, per form (measured, graph of launches, against the
+    // first form's 4 waves, 2 units and 128 waves per CU):
+    //  * plain, when 1-wave workgroups of 2 units cover every unit in one
+    //    pass: W 1, U 2 ([4096, 7168] 17.0 -> 16.3 us);
+    //  * plain, several passes: W 2, U 1, up to 256 waves per CU
+    //    ([32768, 7168] 118.2 -> 112.1 us, [4096, 18432] 40.1 -> 38.3);
+    //  * fused: W 2, U 1, up to 32 waves per CU (one unit: 70.9 -> 67.4 us on
+    //    the gate of [4096, 18432]);
+    //  * gathered rows: W 2, U 2, up to 128 waves per CU (one unit in
+    //    flight: 97 -> 133 us).
+    // Workgroups of 8 or 16 waves were slower on every shape.
+    auto lean = [&](auto w_c, auto u_c, int64_t waves_per_cu) {
+      constexpr int W = decltype(w_c)::value, U = decltype(u_c)::value;
+      const int64_t want_w = (units + W * U - 1) / (W * U);
+      const int64_t cap_w = (int64_t)device_cu_count() * waves_per_cu / W;
       const dim3 gw((unsigned)(want_w < cap_w ? want_w : cap_w)), bw(64 * W);
-      if (fused) hipLaunchKernelGGL((act_quant_lean_kernel<true, false, 64 * W>), gw, bw, 0, stream, a, nbdiv, e);
+      if (fused) hipLaunchKernelGGL((act_quant_lean_kernel<true, false, 64 * W, U>), gw, bw, 0, stream, a, nbdiv, e);
       else if (a.rows != nullptr)
-        hipLaunchKernelGGL((act_quant_lean_kernel<false, true, 64 * W>), gw, bw, 0, stream, a, gdiv, e);
-      else hipLaunchKernelGGL((act_quant_lean_kernel<false, false, 64 * W>), gw, bw, 0, stream, a, nbdiv, e);
+        hipLaunchKernelGGL((act_quant_lean_kernel<false, true, 64 * W, U>), gw, bw, 0, stream, a, gdiv, e);
+      else hipLaunchKernelGGL((act_quant_lean_kernel<false, false, 64 * W, U>), gw, bw, 0, stream, a, nbdiv, e);
       return hipGetLastError();
     };
-    const int64_t one_pass = (units + kUnroll - 1) / kUnroll;  // 1-wave workgroups wanted
-    if (!fused && a.rows == nullptr && one_pass <= (int64_t)device_cu_count() * 32 * (kThreads / 64))
-      return lean(std::integral_constant<int, 64>());
-    return lean(std::integral_constant<int, 128>());
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (fused) return lean(I2(), I1(), 32);
+    if (a.rows != nullptr) return lean(I2(), I2(), 128);
+    if ((units + 1) / 2 <= (int64_t)device_cu_count() * 128) return lean(I1(), I2(), 128);
+    return lean(I2(), I1(), 256);
   }
   if (fused) {
     if (vec) hipLaunchKernelGGL((act_quant_kernel<true, true>), g, blk, 0, stream, a, nb, gdiv, fast);
