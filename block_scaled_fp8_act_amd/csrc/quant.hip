@@ -420,23 +420,36 @@ __global__ __launch_bounds__(kThreads) void weight_dequant_kernel(DequantArgs a)
 // with kDqLeanRows rows per workgroup: 69.5 us against 71.3 us for the
 // general kernel on [18432, 7168] (2 rows measured faster than 4, 8 slower;
 // plain instead of nontemporal stores 5% slower).  Bit-identical results.
+// The workgroup size is chosen per K (dequant_threads): the fewest
+// workgroups of at most 256 threads that cover a row, each thread taking 16
+// columns, so no lane idles where K allows it; against a fixed 256 threads:
+// [18432, 7168] 69.2 -> 63.3 us (224 threads), [36864, 7168] 139.9 -> 126.9,
+// [4096, 2048] 6.3 -> 6.0; [7168, 18432] unchanged.
 constexpr int kDqLeanRows = 2;
+constexpr int kDqMaxThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void weight_dequant_lean_kernel(DequantArgs a, uint32_t wbytes, uint32_t sbytes,
+inline int64_t dequant_threads(int64_t K) {
+  const int64_t chunks = (K + 15) / 16;
+  const int64_t blocks = (chunks + kDqMaxThreads - 1) / kDqMaxThreads;
+  return ((chunks + blocks - 1) / blocks + 15) / 16 * 16;
+}
+
+__global__ __launch_bounds__(kDqMaxThreads) void weight_dequant_lean_kernel(DequantArgs a, uint32_t wbytes, uint32_t sbytes,
                                                                        uint32_t obytes) {
   constexpr int kNt = 2;
+  const uint32_t T = blockDim.x;  // dequant_threads(K)
   const auto rw = buffer_of(a.w, wbytes);
   const auto rs = buffer_of(a.S, sbytes);
   const auto ro = buffer_of(a.out, obytes);
   const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
   const uint32_t ldw = (uint32_t)a.ldw, ldS = (uint32_t)a.ldS, ldo = (uint32_t)a.ldo;
-  const uint32_t cbase = blockIdx.x * (kThreads * 16) + threadIdx.x * 8;
+  const uint32_t cbase = blockIdx.x * (T * 16) + threadIdx.x * 8;
   const uint32_t row0 = blockIdx.y * kDqLeanRows;
   u32x2 w[2][kDqLeanRows];
   float sc[2][kDqLeanRows];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t col = cbase + h * (kThreads * 8);
+    const uint32_t col = cbase + h * (T * 8);
 #pragma unroll
     for (int r = 0; r < kDqLeanRows; ++r) {
       const uint32_t n = row0 + r;
@@ -448,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void weight_dequant_lean_kernel(DequantAr
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t col = cbase + h * (kThreads * 8);
+    const uint32_t col = cbase + h * (T * 8);
 #pragma unroll
     for (int r = 0; r < kDqLeanRows; ++r) {
       const uint32_t n = row0 + r;
@@ -571,8 +584,9 @@ hipError_t launch_weight_dequant(const DequantArgs& a, hipStream_t stream) {
   const int64_t sb = (((a.N - 1) / kBlock) * a.ldS + (a.K - 1) / kBlock + 1) * 4;
   const int64_t lim = (int64_t)1 << 31;
   if (vec && wb < lim && ob < lim && sb < lim) {
-    dim3 g2((unsigned)((a.K + kThreads * 16 - 1) / (kThreads * 16)), (unsigned)((a.N + kDqLeanRows - 1) / kDqLeanRows));
-    hipLaunchKernelGGL(weight_dequant_lean_kernel, g2, dim3(kThreads), 0, stream, a, (uint32_t)wb, (uint32_t)sb,
+    const int64_t T = dequant_threads(a.K);
+    dim3 g2((unsigned)((a.K + T * 16 - 1) / (T * 16)), (unsigned)((a.N + kDqLeanRows - 1) / kDqLeanRows));
+    hipLaunchKernelGGL(weight_dequant_lean_kernel, g2, dim3((unsigned)T), 0, stream, a, (uint32_t)wb, (uint32_t)sb,
                        (uint32_t)ob);
     return hipGetLastError();
   }
