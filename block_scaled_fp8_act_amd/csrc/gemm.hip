@@ -1266,9 +1266,9 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_gemm_kernel(GemmArgs
 //
 // Products with few output tiles (decode rows, the ragged shape) are bound by
 // latency, not by bandwidth or the matrix cores.  gemm_rd_kernel gives each
-// workgroup of kRdWaves waves one 16FM x 16FN output tile and a range of
-// K-blocks; wave w takes the range's K-blocks w, w + kRdWaves, ... (at most
-// DEPTH of them) and issues all of their operand loads at once, so a
+// workgroup of W waves (kRdWaves in every launch) one 16FM x 16FN output tile
+// and a range of K-blocks; wave w takes the range's K-blocks w, w + W, ... (at
+// most DEPTH of them) and issues all of their operand loads at once, so a
 // workgroup needs one memory round trip.  The loads go straight to LDS, each
 // wave into its own slots (one per K-block: the tile's A rows, then its B
 // rows, 128 bytes each in the swizzled layout of the large kernels), as full
