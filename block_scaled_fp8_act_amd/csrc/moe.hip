@@ -164,79 +164,73 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
 
 // ---- combine --------------------------------------------------------------------------
 
-constexpr int kCombineThreads = 64;
+constexpr int kCombineThreads = 256;
 
 __device__ __forceinline__ float bf16_round(float v) { return bf16_lo(pack_bf16x2(v, 0.0f)); }
 
 template <int KMAX>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-  // Workgroup ids run over (token, column block) with the column blocks of a
-  // token adjacent, so a token's k source rows are read start to end by
-  // neighbouring workgroups (grid-stride over the ids for any token count).
-  const int64_t nb = (a.D + kCombineThreads * 8 - 1) / (kCombineThreads * 8);
-  for (int64_t id = blockIdx.x; id < a.T * nb; id += gridDim.x) {
-    const int64_t t = id / nb;
-    const int64_t col = ((id - t * nb) * kCombineThreads + threadIdx.x) * 8;
-    if (col >= a.D) continue;
-    // The token's pairs, sorted by expert (insertion sort, stable).
-    int32_t ex[KMAX], row[KMAX];
-    float w[KMAX];
+  const int64_t t = blockIdx.x;
+  const int64_t col = ((int64_t)blockIdx.y * kCombineThreads + threadIdx.x) * 8;
+  if (col >= a.D) return;
+  // The token's pairs, sorted by expert (insertion sort, stable).
+  int32_t ex[KMAX], row[KMAX];
+  float w[KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool use = j < a.k;
-      ex[j] = use ? a.indices[t * a.ldi + j] : INT32_MAX;
-      row[j] = use ? a.token_rows[t * a.k + j] : -1;
-      w[j] = use ? bf16_lo(a.weights[t * a.ldw + j]) : 0.0f;
+  for (int j = 0; j < KMAX; ++j) {
+    const bool use = j < a.k;
+    ex[j] = use ? a.indices[t * a.ldi + j] : INT32_MAX;
+    row[j] = use ? a.token_rows[t * a.k + j] : -1;
+    w[j] = use ? bf16_lo(a.weights[t * a.ldw + j]) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 1; i < KMAX; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool sw = ex[j] < ex[j - 1];
+      const int32_t e0 = ex[j - 1], r0 = row[j - 1];
+      const float w0 = w[j - 1];
+      ex[j - 1] = sw ? ex[j] : e0;   row[j - 1] = sw ? row[j] : r0;   w[j - 1] = sw ? w[j] : w0;
+      ex[j] = sw ? e0 : ex[j];       row[j] = sw ? r0 : row[j];       w[j] = sw ? w0 : w[j];
     }
+  // All rows' loads in flight before the accumulation.
+  u32x4 v[KMAX];
+  const bool vec = a.vec && col + 8 <= a.D;
 #pragma unroll
-    for (int i = 1; i < KMAX; ++i)
-#pragma unroll
-      for (int j = i; j > 0; --j) {
-        const bool sw = ex[j] < ex[j - 1];
-        const int32_t e0 = ex[j - 1], r0 = row[j - 1];
-        const float w0 = w[j - 1];
-        ex[j - 1] = sw ? ex[j] : e0;   row[j - 1] = sw ? row[j] : r0;   w[j - 1] = sw ? w[j] : w0;
-        ex[j] = sw ? e0 : ex[j];       row[j] = sw ? r0 : row[j];       w[j] = sw ? w0 : w[j];
-      }
-    // All rows' loads in flight before the accumulation.
-    u32x4 v[KMAX];
-    const bool vec = a.vec && col + 8 <= a.D;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (row[j] < 0 || row[j] >= a.R) continue;
-      const uint16_t* src = a.yr + (int64_t)row[j] * a.ldy + col;
-      if (vec) {
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-      } else {
-        uint32_t e[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) e[c] = col + c < a.D ? (uint32_t)src[c] : 0u;
-        v[j] = u32x4{e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16};
-      }
-    }
-    float acc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (row[j] < 0 || row[j] >= a.R) continue;
-      const uint32_t words[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float y = (c & 1) ? bf16_hi(words[c >> 1]) : bf16_lo(words[c >> 1]);
-        acc[c] = bf16_round(acc[c] + bf16_round(y * w[j]));
-      }
-    }
-    uint16_t* dst = a.out + t * a.ldo + col;
+  for (int j = 0; j < KMAX; ++j) {
+    v[j] = u32x4{0u, 0u, 0u, 0u};
+    if (row[j] < 0 || row[j] >= a.R) continue;
+    const uint16_t* src = a.yr + (int64_t)row[j] * a.ldy + col;
     if (vec) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     } else {
+      uint32_t e[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (col + c < a.D) dst[c] = (uint16_t)(pack_bf16x2(acc[c], 0.0f) & 0xffff);
+      for (int c = 0; c < 8; ++c) e[c] = col + c < a.D ? (uint32_t)src[c] : 0u;
+      v[j] = u32x4{e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16};
     }
+  }
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (row[j] < 0 || row[j] >= a.R) continue;
+    const uint32_t words[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float y = (c & 1) ? bf16_hi(words[c >> 1]) : bf16_lo(words[c >> 1]);
+      acc[c] = bf16_round(acc[c] + bf16_round(y * w[j]));
+    }
+  }
+  uint16_t* dst = a.out + t * a.ldo + col;
+  if (vec) {
+    *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (col + c < a.D) dst[c] = (uint16_t)(pack_bf16x2(acc[c], 0.0f) & 0xffff);
   }
 }
 
@@ -276,12 +270,7 @@ hipError_t launch_route(RouteArgs a, hipStream_t stream) {
 hipError_t launch_combine(CombineArgs a, hipStream_t stream) {
   if (a.T == 0 || a.D == 0) return hipSuccess;
   a.vec = aligned(a.yr, 16) && a.ldy % 8 == 0 && aligned(a.out, 16) && a.ldo % 8 == 0;
-  // One wave per workgroup and per 512 columns of a token, the column blocks
-  // of a token adjacent: 98.9 us on the routed-expert combine [32768 -> 4096,
-  // 7168] against 106.8 us for 256 threads with the tokens adjacent (the
-  // fourth block of a 7168-column row half idle).
-  const int64_t ids = a.T * ((a.D + kCombineThreads * 8 - 1) / (kCombineThreads * 8));
-  dim3 g((unsigned)(ids < ((int64_t)1 << 30) ? ids : ((int64_t)1 << 30)));
+  dim3 g((unsigned)a.T, (unsigned)((a.D + kCombineThreads * 8 - 1) / (kCombineThreads * 8)));
   dim3 blk(kCombineThreads);
   if (a.k <= 2) hipLaunchKernelGGL(combine_kernel<2>, g, blk, 0, stream, a);
   else if (a.k <= 4) hipLaunchKernelGGL(combine_kernel<4>, g, blk, 0, stream, a);
