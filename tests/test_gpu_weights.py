@@ -57,7 +57,9 @@ def _stored_weight(N, K, fmt, seed):
 
 
 @pytest.mark.parametrize("N,K,fmt", [(2500, 1000, "ue8m0"), (260, 300, "fp32"), (2048, 7168, "fp32"),
-                                     (2048, 7168, "ue8m0"), (1, 1, "fp32"), (130, 16, "fp32")])
+                                     (2048, 7168, "ue8m0"), (1, 1, "fp32"), (130, 16, "fp32"),
+                                     # workgroups fitted to K: 128 threads, 144 (last one partial), 240 x 5
+                                     (100, 2048, "fp32"), (300, 4112, "fp32"), (200, 18432, "ue8m0")])
 def test_weight_dequant(N, K, fmt):
     q, S = _stored_weight(N, K, fmt, 40 + N)
     out = ds.weight_dequant(dev_u8(q), dev_f32(S))
