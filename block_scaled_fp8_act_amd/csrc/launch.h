@@ -38,7 +38,7 @@ struct RouteArgs {
   int32_t* offsets;        // [E + 1]
   int32_t* row_token;      // [n]
   int32_t* token_rows;     // [T, k] contiguous
-  int32_t* work;           // [E, chunks]
+  int32_t* work;           // [chunks, E]
   int64_t chunk, chunks;   // pairs per chunk, number of chunks
 };
 

@@ -9,7 +9,8 @@
 // torch.where lists them).  Two kernels, no atomics on global memory, so the
 // result is deterministic:
 //   count   -- one workgroup per chunk of pairs, per-expert counts in LDS,
-//              stored expert-major (counts[e][c]);
+//              stored chunk-major (counts[c][e], so that a wave's reads of
+//              one chunk's counts for consecutive experts are contiguous);
 //   scatter -- one workgroup per chunk.  All its threads first reduce the
 //              (small) count table: expert totals, an exclusive scan of them
 //              for the expert offsets, and the counts of earlier chunks, so
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a)
     if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  for (int e = t; e < a.E; e += kRouteThreads) a.work[(int64_t)e * a.chunks + blockIdx.x] = cnt[e];
+  for (int e = t; e < a.E; e += kRouteThreads) a.work[(int64_t)blockIdx.x * a.E + e] = cnt[e];
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a) {
@@ -74,18 +75,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
   const int t = threadIdx.x;
   const int c = blockIdx.x;
   // Per expert: the total over all chunks and the part in chunks before this
-  // one.  A row of the table (at most kMaxRouteChunks entries) is loaded at
-  // once.  A thread's experts are contiguous, so the exclusive scan of the
-  // totals is a per-thread sum plus a block scan.
+  // one.  An expert's counts in every chunk (at most kMaxRouteChunks) are
+  // loaded at once; consecutive threads take consecutive experts, so each
+  // load instruction reads one contiguous stretch of a chunk's row.  A
+  // thread's experts are contiguous, so the exclusive scan of the totals is
+  // a per-thread sum plus a block scan.
   const int per = (a.E + kRouteThreads - 1) / kRouteThreads;
   const int e0 = t * per < a.E ? t * per : a.E;
   const int e1 = e0 + per < a.E ? e0 + per : a.E;
   int32_t tsum = 0;
   for (int e = e0; e < e1; ++e) {
-    const int32_t* row = a.work + (int64_t)e * a.chunks;
     int32_t v[kMaxRouteChunks];
 #pragma unroll
-    for (int j = 0; j < kMaxRouteChunks; ++j) v[j] = j < a.chunks ? row[j] : 0;
+    for (int j = 0; j < kMaxRouteChunks; ++j) v[j] = j < a.chunks ? a.work[(int64_t)j * a.E + e] : 0;
     int32_t tot = 0, before = 0;
 #pragma unroll
     for (int j = 0; j < kMaxRouteChunks; ++j) {
