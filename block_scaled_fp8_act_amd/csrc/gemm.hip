@@ -909,18 +909,26 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t pid, int64_t total) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// x / d for x >= 0, d > 0 (tile-index arithmetic at the start of a tile):
+// the 32-bit division whenever both fit, since a 64-bit integer division is
+// a long instruction sequence that delays the tile's first loads.
+__device__ __forceinline__ int64_t div_u(int64_t x, int64_t d) {
+  if ((uint64_t)(x | d) <= 0xffffffffull) return (int64_t)((uint32_t)x / (uint32_t)d);
+  return x / d;
+}
+
 // Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges, then
 // GROUP_M-row groups inside a range.
 __device__ __forceinline__ void tile_of(int64_t pid, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
   const int64_t total = tiles_m * tiles_n;
   pid = xcd_contiguous(pid, total);
   const int64_t per_group = (int64_t)kGroupM * tiles_n;
-  const int64_t gid = pid / per_group;
+  const int64_t gid = div_u(pid, per_group);
   const int64_t first_m = gid * kGroupM;
   const int64_t gsize = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
-  const int64_t in = pid % per_group;
-  tm = first_m + in % gsize;
-  tn = in / gsize;
+  const int64_t in = pid - gid * per_group;
+  tn = div_u(in, gsize);
+  tm = first_m + (in - tn * gsize);
 }
 
 // VEC > 0: the register-staged pipeline with VEC-byte loads (any alignment;
@@ -1763,22 +1771,37 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmArgs p) {
 // expert's activation rows and weight panels in its L2.  pid is the
 // workgroup's index within its launch range, which starts at a multiple of 8
 // (so pid % 8 is still its XCD).
+// The last expert e in [0, E) with ts[e] <= slot, for ts non-decreasing and
+// ts[0] <= slot < ts[E]: each round the wave's 64 lanes test 64 evenly
+// spaced candidates at once and a ballot keeps the bracket between the last
+// one at or below slot and the next, so up to 4096 experts take two rounds
+// of loads where a bisection takes twelve dependent ones.
+__device__ __forceinline__ int64_t find_expert(const int32_t* ts, int64_t E, int64_t slot) {
+  const int lane = lane_id();
+  int64_t lo = 0, hi = E;  // invariant: ts[lo] <= slot < ts[hi]
+  while (hi - lo > 1) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t i = lo + (int64_t)lane * step;
+    const bool ok = i < hi && ts[i] <= slot;  // true on a prefix of the lanes, lane 0 included
+    const uint64_t m = __ballot(ok);
+    const int64_t nlo = lo + (int64_t)(63 - __builtin_clzll(m)) * step;
+    hi = nlo + step < hi ? nlo + step : hi;
+    lo = nlo;
+  }
+  return lo;
+}
+
+// class_tiles: the class's row-tile count ts[E] when the caller has loaded
+// it already (negative: load it here).
 template <class CF, int VEC, bool GLU>
-__device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uint8_t* smem) {
+__device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uint8_t* smem, int64_t class_tiles = -1) {
   const int32_t* ts = p.tile_start;
   const int64_t tiles_n = col_tiles<CF, GLU>(p);
-  const int64_t total = (int64_t)ts[p.E] * tiles_n;
+  const int64_t total = (class_tiles >= 0 ? class_tiles : (int64_t)ts[p.E]) * tiles_n;
   if (pid >= total) return;
   const int64_t L = xcd_contiguous(pid, total);
-  const int64_t slot0 = L / tiles_n;
-  // Last expert e with ts[e] <= slot0; then ts[e+1] > slot0.
-  int64_t lo = 0, hi = p.E;  // invariant: ts[lo] <= slot0 < ts[hi]
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (ts[mid] <= slot0) lo = mid;
-    else hi = mid;
-  }
-  const int64_t e = lo;
+  const int64_t slot0 = div_u(L, tiles_n);
+  const int64_t e = find_expert(ts, p.E, slot0);
   // Expert e's row tiles x column tiles are one contiguous id range; inside
   // it the ids run in groups of up to kGroupM row tiles, row tile fastest,
   // so the concurrent tiles of a large expert share each weight panel as
@@ -1786,11 +1809,11 @@ __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uin
   const int64_t rt = ts[e + 1] - ts[e];
   const int64_t l = L - (int64_t)ts[e] * tiles_n;
   const int64_t per_group = (int64_t)kGroupM * tiles_n;
-  const int64_t g0 = l / per_group * kGroupM;
+  const int64_t g0 = div_u(l, per_group) * kGroupM;
   const int64_t gsize = rt - g0 < kGroupM ? rt - g0 : kGroupM;
   const int64_t in = l - g0 * tiles_n;
-  const int64_t slot = ts[e] + g0 + in % gsize;
-  const int64_t tn = in / gsize;
+  const int64_t tn = div_u(in, gsize);
+  const int64_t slot = ts[e] + g0 + (in - tn * gsize);
   int64_t r0, r1;
   expert_rows(p.offsets, e, p.M, r0, r1);
   const int64_t kbn = (p.N + BK - 1) / BK;
@@ -1837,10 +1860,10 @@ __global__ __launch_bounds__(C2::kThreads) void grouped_merged_kernel(GemmArgs p
   constexpr int LDS = L01 > C2::LDS_BYTES ? L01 : C2::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   const int64_t tiles_n = col_tiles<C2, GLU>(p);
-  auto chunks_of = [&](int c) __attribute__((always_inline)) {
-    return ((int64_t)p.tile_start[c * (p.E + 1) + p.E] * tiles_n + kXcds - 1) / kXcds;
-  };
-  const int64_t c0 = chunks_of(0), c1 = chunks_of(1), c2 = chunks_of(2);
+  const int64_t t0 = p.tile_start[p.E], t1 = p.tile_start[(p.E + 1) + p.E],
+                t2 = p.tile_start[2 * (p.E + 1) + p.E];  // row tiles per class
+  auto chunks_of = [&](int64_t t) __attribute__((always_inline)) { return (t * tiles_n + kXcds - 1) / kXcds; };
+  const int64_t c0 = chunks_of(t0), c1 = chunks_of(t1), c2 = chunks_of(t2);
   const int64_t C = c0 + c1 + c2;
   const int64_t q = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
   if (q >= C) return;
@@ -1849,15 +1872,15 @@ __global__ __launch_bounds__(C2::kThreads) void grouped_merged_kernel(GemmArgs p
   if (span < 1) span = 1;
   GemmArgs a = p;
   int64_t local;
-  const int64_t b2 = q < span ? (q + 1) * c2 / span : c2;  // class-2 chunks at positions <= q
-  if (q < span && b2 > q * c2 / span) {
+  const int64_t b2 = q < span ? div_u((q + 1) * c2, span) : c2;  // class-2 chunks at positions <= q
+  if (q < span && b2 > div_u(q * c2, span)) {
     a.grp_class = 2;
     a.tile_start = p.tile_start + 2 * (p.E + 1);
     local = b2 - 1;
   } else {
     const int64_t r = q - b2, cr = C - c2;  // rank among the other chunks (cr > 0 here)
-    const int64_t b1 = (r + 1) * c1 / cr;
-    if (b1 > r * c1 / cr) {
+    const int64_t b1 = div_u((r + 1) * c1, cr);
+    if (b1 > div_u(r * c1, cr)) {
       a.grp_class = 1;
       a.tile_start = p.tile_start + (p.E + 1);
       local = b1 - 1;
@@ -1867,9 +1890,9 @@ __global__ __launch_bounds__(C2::kThreads) void grouped_merged_kernel(GemmArgs p
     }
   }
   const int64_t pid = local * kXcds + x;
-  if (a.grp_class == 2) grouped_tile<C2, VEC, GLU>(a, pid, smem);
-  else if (a.grp_class == 1) grouped_tile<C1, VEC, GLU>(a, pid, smem);
-  else grouped_tile<C0, VEC, GLU>(a, pid, smem);
+  if (a.grp_class == 2) grouped_tile<C2, VEC, GLU>(a, pid, smem, t2);
+  else if (a.grp_class == 1) grouped_tile<C1, VEC, GLU>(a, pid, smem, t1);
+  else grouped_tile<C0, VEC, GLU>(a, pid, smem, t0);
 }
 
 inline bool aligned(const void* q, size_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; }
@@ -2183,18 +2206,23 @@ hipError_t grouped_classes(const GemmArgs& a, hipStream_t stream) {
   const int64_t E = a.E, M = a.M;
   auto tiles_n = [&](int bn) { return GLU ? a.glu_f / BK : (a.N + bn - 1) / bn; };
   auto mn = [](int64_t x, int64_t y) { return x < y ? x : y; };
-  // Bounds on each class's row tiles: at most one per expert with at least 1
-  // (class 0) or C0::BM + 1 (class 1) rows; for the large class at most
-  // M/C2::BM whole tiles plus one padded tile per expert with > C1::BM rows.
+  // Bounds on the row tiles (the counts are on the device): a non-empty
+  // expert has at most one tile of class 0 or 1 (its only tile, or the
+  // remainder after its whole C2::BM-row tiles), so classes 0 and 1 together
+  // have at most min(E, M); the large class at most M/C2::BM whole tiles
+  // plus one padded tile per expert with > C1::BM rows.
   GemmArgs c0 = s;
   c0.grp_class = 0;
-  const int64_t s0 = mn(E, M), s1 = mn(E, M / (C0::BM + 1));
+  static_assert(C0::BN == C1::BN && C1::BN == C2::BN, "one column tiling");
+  const int64_t s01 = mn(E, M);
   const int64_t s2 = (M + C2::BM - 1) / C2::BM + mn(E, M / (C1::BM + 1));
-  auto up8 = [](int64_t v) { return (v + 7) / 8 * 8; };
-  const int64_t n2 = up8(s2 * tiles_n(C2::BN)), n1 = up8(s1 * tiles_n(C1::BN)), n0 = up8(s0 * tiles_n(C0::BN));
-  // One workgroup per possible tile of each class (a bound: the counts are on
-  // the device); the kernel maps ids to the actual tiles.
-  const dim3 grid((unsigned)(n2 + n1 + n0)), blk(C2::kThreads);
+  // One workgroup per possible tile, in chunks of 8: each class rounds its
+  // tiles up to whole chunks, which classes 0 and 1 together take at most
+  // one chunk more than their joint bound.  The kernel maps chunks to the
+  // actual tiles and the rest exit.
+  const int64_t tn = tiles_n(C2::BN);
+  const int64_t chunks = (s01 * tn + 7) / 8 + 1 + (s2 * tn + 7) / 8;
+  const dim3 grid((unsigned)(chunks * 8)), blk(C2::kThreads);
   const bool kfull = a.K % BK == 0;
   const int64_t pct = tall_span_pct(a.K);
   if (a.pow2) {
