@@ -234,14 +234,21 @@ dsfp8_status dsfp8_gemm(const void* A, int64_t lda, const float* a_s, int64_t as
 }
 
 size_t dsfp8_grouped_gemm_workspace_bytes(int64_t E, int64_t M_total, int64_t N, int64_t K) {
-  (void)M_total;
-  (void)N;
   (void)K;
-  if (E < 1 || E > kMaxExperts) return 0;
-  return dsfp8::grouped_workspace_bytes(E);
+  if (E < 1 || E > kMaxExperts || !dim_ok(M_total) || !dim_ok(N)) return 0;
+  return dsfp8::grouped_workspace_bytes(E, M_total, N);
 }
 
 namespace {
+
+// The workspace of a grouped launch: the tile schedule, then (when the
+// workspace is 16-byte aligned for its int4 entries) the tile plan.
+void grouped_workspace(dsfp8::GemmArgs& a, void* workspace) {
+  a.tile_start = static_cast<int32_t*>(workspace);
+  a.tile_plan = al(workspace, 16) ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
+                                                               dsfp8::grouped_schedule_bytes(a.E))
+                                  : nullptr;
+}
 
 // Arguments of the grouped product (everything but the workspace).
 dsfp8_status grouped_args(const void* A, int64_t lda, const float* a_s, int64_t as_row_stride,
@@ -294,7 +301,7 @@ dsfp8_status dsfp8_grouped_gemm(const void* A, int64_t lda, const float* a_s, in
   if (workspace_bytes < need) return DSFP8_ERR_WORKSPACE;
   if (need > 0 && workspace == nullptr) return DSFP8_ERR_NULL;
   if (!al(workspace, 4)) return DSFP8_ERR_ALIGN;
-  a.tile_start = static_cast<int32_t*>(workspace);
+  grouped_workspace(a, workspace);
   return launched(dsfp8::launch_grouped_gemm(a, stream));
 }
 
@@ -384,7 +391,7 @@ dsfp8_status grouped_glu(const void* A, int64_t a_rows, int64_t lda, const float
   if (M_total == 0 || F == 0) return DSFP8_OK;
   a.offsets = offsets;
   a.E = E;
-  a.tile_start = static_cast<int32_t*>(workspace);
+  grouped_workspace(a, workspace);
   return launched(dsfp8::launch_grouped_gemm_glu(a, stream));
 }
 

@@ -1764,6 +1764,42 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmArgs p) {
   }
 }
 
+// The last expert e in [0, E) with ts[e] <= slot, for ts non-decreasing and
+// ts[0] <= slot < ts[E].  UNIFORM (slot the same in every lane of the wave):
+// each round the wave's 64 lanes test 64 evenly spaced candidates at once and
+// a ballot keeps the bracket between the last one at or below slot and the
+// next, so up to 4096 experts take two rounds of loads where a bisection
+// takes twelve dependent ones.  Otherwise each lane bisects on its own.
+template <bool UNIFORM>
+__device__ __forceinline__ int64_t find_expert(const int32_t* ts, int64_t E, int64_t slot) {
+  int64_t lo = 0, hi = E;  // invariant: ts[lo] <= slot < ts[hi]
+  if constexpr (UNIFORM) {
+    const int lane = lane_id();
+    while (hi - lo > 1) {
+      const int64_t step = (hi - lo + 63) / 64;
+      const int64_t i = lo + (int64_t)lane * step;
+      const bool ok = i < hi && ts[i] <= slot;  // true on a prefix of the lanes, lane 0 included
+      const uint64_t m = __ballot(ok);
+      const int64_t nlo = lo + (int64_t)(63 - __builtin_clzll(m)) * step;
+      hi = nlo + step < hi ? nlo + step : hi;
+      lo = nlo;
+    }
+  } else {
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (ts[mid] <= slot) lo = mid;
+      else hi = mid;
+    }
+  }
+  return lo;
+}
+
+// One row tile x column tile of a grouped product: expert e, rows
+// [row0, row_end) of A and C (at most the class's tile height), column tile tn.
+struct GroupedSlot {
+  int64_t e, row0, row_end, tn;
+};
+
 // One workgroup per (row tile of an expert, column tile).  The grid is sized
 // for the worst case; the real number of row tiles is ts[E].  Ids past the
 // real work exit at once; the rest are renumbered XCD-contiguously over the
@@ -1771,37 +1807,20 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmArgs p) {
 // expert's activation rows and weight panels in its L2.  pid is the
 // workgroup's index within its launch range, which starts at a multiple of 8
 // (so pid % 8 is still its XCD).
-// The last expert e in [0, E) with ts[e] <= slot, for ts non-decreasing and
-// ts[0] <= slot < ts[E]: each round the wave's 64 lanes test 64 evenly
-// spaced candidates at once and a ballot keeps the bracket between the last
-// one at or below slot and the next, so up to 4096 experts take two rounds
-// of loads where a bisection takes twelve dependent ones.
-__device__ __forceinline__ int64_t find_expert(const int32_t* ts, int64_t E, int64_t slot) {
-  const int lane = lane_id();
-  int64_t lo = 0, hi = E;  // invariant: ts[lo] <= slot < ts[hi]
-  while (hi - lo > 1) {
-    const int64_t step = (hi - lo + 63) / 64;
-    const int64_t i = lo + (int64_t)lane * step;
-    const bool ok = i < hi && ts[i] <= slot;  // true on a prefix of the lanes, lane 0 included
-    const uint64_t m = __ballot(ok);
-    const int64_t nlo = lo + (int64_t)(63 - __builtin_clzll(m)) * step;
-    hi = nlo + step < hi ? nlo + step : hi;
-    lo = nlo;
-  }
-  return lo;
-}
-
-// class_tiles: the class's row-tile count ts[E] when the caller has loaded
-// it already (negative: load it here).
-template <class CF, int VEC, bool GLU>
-__device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uint8_t* smem, int64_t class_tiles = -1) {
+//
+// The tile of workgroup pid of class p.grp_class (p.tile_start is that
+// class's schedule, tile height BM).  class_tiles: the class's row-tile count
+// ts[E] when the caller has loaded it already (negative: load it here).
+// False for ids past the class's tiles.
+template <int BM, bool UNIFORM>
+__device__ __forceinline__ bool grouped_slot(const GemmArgs& p, int64_t pid, int64_t tiles_n, int64_t class_tiles,
+                                             GroupedSlot& out) {
   const int32_t* ts = p.tile_start;
-  const int64_t tiles_n = col_tiles<CF, GLU>(p);
   const int64_t total = (class_tiles >= 0 ? class_tiles : (int64_t)ts[p.E]) * tiles_n;
-  if (pid >= total) return;
+  if (pid >= total) return false;
   const int64_t L = xcd_contiguous(pid, total);
   const int64_t slot0 = div_u(L, tiles_n);
-  const int64_t e = find_expert(ts, p.E, slot0);
+  const int64_t e = find_expert<UNIFORM>(ts, p.E, slot0);
   // Expert e's row tiles x column tiles are one contiguous id range; inside
   // it the ids run in groups of up to kGroupM row tiles, row tile fastest,
   // so the concurrent tiles of a large expert share each weight panel as
@@ -1816,17 +1835,26 @@ __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uin
   const int64_t slot = ts[e] + g0 + (in - tn * gsize);
   int64_t r0, r1;
   expert_rows(p.offsets, e, p.M, r0, r1);
+  int64_t clo, chi;
+  class_rows(r1 - r0, p.grp_class, p.grp_classes, p.grp_h, clo, chi);
+  out.e = e;
+  out.row0 = r0 + clo + (slot - ts[e]) * BM;
+  out.row_end = r0 + chi;
+  out.tn = tn;
+  return true;
+}
+
+template <class CF, int VEC, bool GLU>
+__device__ __forceinline__ void grouped_run(const GemmArgs& p, const GroupedSlot& g, uint8_t* smem) {
   const int64_t kbn = (p.N + BK - 1) / BK;
   TileRef t;
   t.A = p.A;
   t.a_s = p.a_s;
-  t.B = p.B + e * p.N * p.ldb;
-  t.b_s = p.b_s + e * kbn * p.ldbs;
-  int64_t clo, chi;
-  class_rows(r1 - r0, p.grp_class, p.grp_classes, p.grp_h, clo, chi);
-  t.row0 = r0 + clo + (slot - ts[e]) * CF::BM;
-  t.row_end = r0 + chi;
-  t.n0 = tn * kColStep<CF, GLU>;
+  t.B = p.B + g.e * p.N * p.ldb;
+  t.b_s = p.b_s + g.e * kbn * p.ldbs;
+  t.row0 = g.row0;
+  t.row_end = g.row_end;
+  t.n0 = g.tn * kColStep<CF, GLU>;
   t.kb0 = 0;
   t.kb1 = (int)((p.K + BK - 1) / BK);
   t.partial = nullptr;
@@ -1836,22 +1864,92 @@ __device__ __forceinline__ void grouped_tile(const GemmArgs& p, int64_t pid, uin
 template <class CF, int VEC, bool GLU = false>
 __global__ __launch_bounds__(CF::kThreads) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[CF::LDS_BYTES];
-  grouped_tile<CF, VEC, GLU>(p, blockIdx.x, smem);
+  GroupedSlot g;
+  if (grouped_slot<CF::BM, true>(p, blockIdx.x, col_tiles<CF, GLU>(p), -1, g)) grouped_run<CF, VEC, GLU>(p, g, smem);
 }
 
 // The three tile classes of a grouped product in one launch.  Workgroup ids
 // go in chunks of 8 (one per XCD, so a class's local id keeps the XCD of the
-// workgroup and grouped_tile's XCD-contiguous ranges hold).  From the tile
+// workgroup and grouped_slot's XCD-contiguous ranges hold).  From the tile
 // counts the schedule kernel wrote, chunk q belongs to class 2 (the 256-row
 // tiles, compute-bound) at evenly spread positions over the first `pct`
 // percent of the chunks, and the other chunks to classes 1 and 0 (64- and
 // 128-row tiles, bound by streaming their experts' weights) evenly over all
 // positions.  The CUs then run both kinds at once, so the weight stream of
 // the small experts overlaps the products of the large ones.  Chunks past
-// the last tile exit.  p holds the class-0 schedule; class c's is c*(E+1)
-// later.  All three classes use 8 waves, 256-column tiles and one workgroup
-// per CU (their LDS rings take 125 to 149 KB), so sharing one kernel costs
-// no occupancy.
+// the last tile have no class.  p.tile_start holds the class-0 schedule;
+// class c's is c*(E+1) later.  Returns the class (-1: none) and the id within
+// the class.
+__device__ __forceinline__ int merged_class(const GemmArgs& p, int64_t bid, int64_t tiles_n, int64_t pct,
+                                            const int64_t (&tc)[3], int64_t& pid) {
+  auto chunks_of = [&](int64_t t) __attribute__((always_inline)) { return (t * tiles_n + kXcds - 1) / kXcds; };
+  const int64_t c0 = chunks_of(tc[0]), c1 = chunks_of(tc[1]), c2 = chunks_of(tc[2]);
+  const int64_t C = c0 + c1 + c2;
+  const int64_t q = bid / kXcds, x = bid % kXcds;
+  if (q >= C) return -1;
+  int64_t span = C * pct / 100;
+  if (span < c2) span = c2;
+  if (span < 1) span = 1;
+  int c;
+  int64_t local;
+  const int64_t b2 = q < span ? div_u((q + 1) * c2, span) : c2;  // class-2 chunks at positions <= q
+  if (q < span && b2 > div_u(q * c2, span)) {
+    c = 2;
+    local = b2 - 1;
+  } else {
+    const int64_t r = q - b2, cr = C - c2;  // rank among the other chunks (cr > 0 here)
+    const int64_t b1 = div_u((r + 1) * c1, cr);
+    if (b1 > div_u(r * c1, cr)) {
+      c = 1;
+      local = b1 - 1;
+    } else {
+      c = 0;
+      local = r - b1;
+    }
+  }
+  pid = local * kXcds + x;
+  return c;
+}
+
+// The tile of merged-launch workgroup bid (false: none).
+template <class C0, class C1, class C2, bool GLU, bool UNIFORM>
+__device__ __forceinline__ bool merged_slot(const GemmArgs& p, int64_t bid, int64_t pct, int& c, GroupedSlot& g) {
+  const int64_t tiles_n = col_tiles<C2, GLU>(p);
+  const int64_t tc[3] = {p.tile_start[p.E], p.tile_start[(p.E + 1) + p.E], p.tile_start[2 * (p.E + 1) + p.E]};
+  int64_t pid;
+  c = merged_class(p, bid, tiles_n, pct, tc, pid);
+  if (c < 0) return false;
+  GemmArgs a = p;
+  a.grp_class = c;
+  a.tile_start = p.tile_start + c * (p.E + 1);
+  if (c == 2) return grouped_slot<C2::BM, UNIFORM>(a, pid, tiles_n, tc[2], g);
+  if (c == 1) return grouped_slot<C1::BM, UNIFORM>(a, pid, tiles_n, tc[1], g);
+  return grouped_slot<C0::BM, UNIFORM>(a, pid, tiles_n, tc[0], g);
+}
+
+// The merged launch's tile of every workgroup id, computed ahead of it by one
+// thread per id: int4 {expert (-1: no tile), first row, row end, column tile
+// * 4 + class}.  A workgroup of the merged launch then finds its tile with one
+// 16-byte load instead of the dependent loads of the class totals, the
+// expert search and the expert's rows, which delay every tile's first weight
+// load by about 2 us (13% of a 64-row tile of the routed-expert
+// down-projection).
+template <class C0, class C1, class C2, bool GLU>
+__global__ __launch_bounds__(256) void tile_plan_kernel(GemmArgs p, int64_t pct, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  int c = -1;
+  GroupedSlot g;
+  int4 v = make_int4(-1, 0, 0, 0);
+  if (merged_slot<C0, C1, C2, GLU, false>(p, i, pct, c, g))
+    v = make_int4((int)g.e, (int)g.row0, (int)g.row_end, (int)(g.tn * 4 + c));
+  reinterpret_cast<int4*>(p.tile_plan)[i] = v;
+}
+
+// All three classes use 8 waves, 256-column tiles and one workgroup per CU
+// (their LDS rings take 125 to 149 KB), so sharing one kernel costs no
+// occupancy.  With p.tile_plan each workgroup reads its tile from the plan;
+// without it (a caller without room for the plan) it maps its id itself.
 template <class C0, class C1, class C2, int VEC, bool GLU>
 __global__ __launch_bounds__(C2::kThreads) void grouped_merged_kernel(GemmArgs p, int64_t pct) {
   static_assert(C0::kThreads == C2::kThreads && C1::kThreads == C2::kThreads, "one workgroup size");
@@ -1859,40 +1957,22 @@ __global__ __launch_bounds__(C2::kThreads) void grouped_merged_kernel(GemmArgs p
   constexpr int L01 = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
   constexpr int LDS = L01 > C2::LDS_BYTES ? L01 : C2::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int64_t tiles_n = col_tiles<C2, GLU>(p);
-  const int64_t t0 = p.tile_start[p.E], t1 = p.tile_start[(p.E + 1) + p.E],
-                t2 = p.tile_start[2 * (p.E + 1) + p.E];  // row tiles per class
-  auto chunks_of = [&](int64_t t) __attribute__((always_inline)) { return (t * tiles_n + kXcds - 1) / kXcds; };
-  const int64_t c0 = chunks_of(t0), c1 = chunks_of(t1), c2 = chunks_of(t2);
-  const int64_t C = c0 + c1 + c2;
-  const int64_t q = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
-  if (q >= C) return;
-  int64_t span = C * pct / 100;
-  if (span < c2) span = c2;
-  if (span < 1) span = 1;
-  GemmArgs a = p;
-  int64_t local;
-  const int64_t b2 = q < span ? div_u((q + 1) * c2, span) : c2;  // class-2 chunks at positions <= q
-  if (q < span && b2 > div_u(q * c2, span)) {
-    a.grp_class = 2;
-    a.tile_start = p.tile_start + 2 * (p.E + 1);
-    local = b2 - 1;
-  } else {
-    const int64_t r = q - b2, cr = C - c2;  // rank among the other chunks (cr > 0 here)
-    const int64_t b1 = div_u((r + 1) * c1, cr);
-    if (b1 > div_u(r * c1, cr)) {
-      a.grp_class = 1;
-      a.tile_start = p.tile_start + (p.E + 1);
-      local = b1 - 1;
-    } else {
-      a.grp_class = 0;
-      local = r - b1;
-    }
+  int c;
+  GroupedSlot g;
+  if (p.tile_plan != nullptr) {
+    const int4 v = reinterpret_cast<const int4*>(p.tile_plan)[blockIdx.x];
+    if (v.x < 0) return;
+    g.e = v.x;
+    g.row0 = v.y;
+    g.row_end = v.z;
+    g.tn = v.w >> 2;
+    c = v.w & 3;
+  } else if (!merged_slot<C0, C1, C2, GLU, true>(p, blockIdx.x, pct, c, g)) {
+    return;
   }
-  const int64_t pid = local * kXcds + x;
-  if (a.grp_class == 2) grouped_tile<C2, VEC, GLU>(a, pid, smem, t2);
-  else if (a.grp_class == 1) grouped_tile<C1, VEC, GLU>(a, pid, smem, t1);
-  else grouped_tile<C0, VEC, GLU>(a, pid, smem, t0);
+  if (c == 2) grouped_run<C2, VEC, GLU>(p, g, smem);
+  else if (c == 1) grouped_run<C1, VEC, GLU>(p, g, smem);
+  else grouped_run<C0, VEC, GLU>(p, g, smem);
 }
 
 inline bool aligned(const void* q, size_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; }
@@ -2181,6 +2261,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   return dispatch<CfgDma, Cfg128, false>(a, dense_grid<CfgDma>(a), dense_grid<Cfg128>(a), stream);
 }
 
+// Tile heights of the merged grouped launch's three classes.
+constexpr int kGrpH0 = 64, kGrpH1 = 128, kGrpH2 = 256;
+
+// Workgroups of a merged grouped launch over E experts, M rows and tn column
+// tiles (a bound: the tile counts are on the device).  A non-empty expert has
+// at most one tile of class 0 or 1 (its only tile, or the remainder after its
+// whole 256-row tiles), so classes 0 and 1 together have at most min(E, M);
+// the large class at most M/256 whole tiles plus one padded tile per expert
+// with more than 128 rows.  Ids go in chunks of 8: each class rounds its
+// tiles up to whole chunks, which classes 0 and 1 together take at most one
+// chunk more than their joint bound.  The kernel maps chunks to the actual
+// tiles and the rest exit.
+int64_t merged_workgroups(int64_t E, int64_t M, int64_t tn) {
+  auto mn = [](int64_t x, int64_t y) { return x < y ? x : y; };
+  const int64_t s01 = mn(E, M);
+  const int64_t s2 = (M + kGrpH2 - 1) / kGrpH2 + mn(E, M / (kGrpH1 + 1));
+  return ((s01 * tn + 7) / 8 + 1 + (s2 * tn + 7) / 8) * 8;
+}
+
 // Spread of the 256-row tiles over a grouped launch (percent of its chunks):
 // measured on the routed-expert products, mixing them with the small-expert
 // tiles over the whole launch made the down-projection (K = 2048) 3.3% faster
@@ -2203,28 +2302,20 @@ hipError_t grouped_classes(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, stream, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t E = a.E, M = a.M;
-  auto tiles_n = [&](int bn) { return GLU ? a.glu_f / BK : (a.N + bn - 1) / bn; };
-  auto mn = [](int64_t x, int64_t y) { return x < y ? x : y; };
-  // Bounds on the row tiles (the counts are on the device): a non-empty
-  // expert has at most one tile of class 0 or 1 (its only tile, or the
-  // remainder after its whole C2::BM-row tiles), so classes 0 and 1 together
-  // have at most min(E, M); the large class at most M/C2::BM whole tiles
-  // plus one padded tile per expert with > C1::BM rows.
+  static_assert(C0::BN == C1::BN && C1::BN == C2::BN, "one column tiling");
+  static_assert(C0::BM == kGrpH0 && C1::BM == kGrpH1 && C2::BM == kGrpH2, "the heights the grid bound assumes");
   GemmArgs c0 = s;
   c0.grp_class = 0;
-  static_assert(C0::BN == C1::BN && C1::BN == C2::BN, "one column tiling");
-  const int64_t s01 = mn(E, M);
-  const int64_t s2 = (M + C2::BM - 1) / C2::BM + mn(E, M / (C1::BM + 1));
-  // One workgroup per possible tile, in chunks of 8: each class rounds its
-  // tiles up to whole chunks, which classes 0 and 1 together take at most
-  // one chunk more than their joint bound.  The kernel maps chunks to the
-  // actual tiles and the rest exit.
-  const int64_t tn = tiles_n(C2::BN);
-  const int64_t chunks = (s01 * tn + 7) / 8 + 1 + (s2 * tn + 7) / 8;
-  const dim3 grid((unsigned)(chunks * 8)), blk(C2::kThreads);
+  const int64_t n = merged_workgroups(a.E, a.M, GLU ? a.glu_f / BK : (a.N + C2::BN - 1) / C2::BN);
+  const dim3 grid((unsigned)n), blk(C2::kThreads);
   const bool kfull = a.K % BK == 0;
   const int64_t pct = tall_span_pct(a.K);
+  if (c0.tile_plan != nullptr) {
+    hipLaunchKernelGGL((tile_plan_kernel<C0, C1, C2, GLU>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, c0,
+                       pct, n);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (a.pow2) {
     if (kfull) hipLaunchKernelGGL((grouped_merged_kernel<C0, C1, C2, -2, GLU>), grid, blk, 0, stream, c0, pct);
     else hipLaunchKernelGGL((grouped_merged_kernel<C0, C1, C2, -3, GLU>), grid, blk, 0, stream, c0, pct);
@@ -2282,11 +2373,16 @@ hipError_t launch_grouped_gemm_glu(const GemmArgs& a, hipStream_t stream) {
   return grouped_classes<CfgGlu64, CfgGlu128, CfgDmaBig, true>(a, stream);
 }
 
-size_t grouped_workspace_bytes(int64_t E) {
+size_t grouped_schedule_bytes(int64_t E) {
   const size_t n = (size_t)kMaxClasses * (size_t)(E + 1) * sizeof(int32_t);
   return (n + 255) & ~(size_t)255;
 }
 
+size_t grouped_workspace_bytes(int64_t E, int64_t M, int64_t N) {
+  // the schedule, then the tile plan: one int4 per workgroup of the merged
+  // launch (N / 256 column tiles; the gated form passes N = 2F)
+  return grouped_schedule_bytes(E) + (size_t)merged_workgroups(E, M, (N + 255) / 256) * sizeof(int4);
+}
 }  // namespace dsfp8
 
 // ---- allocation-free grouped product ------------------------------------------

@@ -93,6 +93,9 @@ struct GemmArgs {
   const int32_t* offsets;
   int64_t E;
   int32_t* tile_start;  // workspace: E+1 ints (this launch's tile class)
+  // workspace after the schedule: the merged launch's tile of every
+  // workgroup, 4 ints each (NULL: each workgroup maps its id itself)
+  int32_t* tile_plan;
   // tile classes of the grouped launches: this launch's class, the number of
   // classes and their row-tile heights (increasing)
   int grp_class, grp_classes;
@@ -133,7 +136,9 @@ hipError_t launch_weight_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 
-size_t grouped_workspace_bytes(int64_t E);
+size_t grouped_schedule_bytes(int64_t E);
+size_t grouped_workspace_bytes(int64_t E, int64_t M, int64_t N);
+int64_t merged_workgroups(int64_t E, int64_t M, int64_t tn);
 
 // The grouped product with its tile schedule in a static device array of
 // 3 * (kNoAllocMaxExperts + 1) int32 per GPU instead of a caller workspace

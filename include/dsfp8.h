@@ -238,6 +238,12 @@ size_t dsfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *            outside A, a_s or C.  Experts with no rows cost nothing.
  *   C        bf16 [M_total, N], row stride ldc              (device, written)
  *   scale_fmt  as for dsfp8_gemm.
+ *   workspace  at least dsfp8_grouped_gemm_workspace_bytes(E, M_total, N, K)
+ *            bytes of device memory, 4-byte aligned (scratch: the per-expert
+ *            tile schedule, then, if 16-byte aligned, a table of every
+ *            workgroup's tile that saves each tile a chain of dependent
+ *            loads; its size grows with E, M_total and N / 256).  Its
+ *            contents need no initialisation and are rewritten by every call.
  * The combine step (scatter-add of each row times its routing weight) is not
  * part of this call.
  * Errors: NULL, SHAPE (E < 1, or E > 65536), LD, ALIGN, SCALE_FMT, WORKSPACE,
