@@ -157,3 +157,51 @@ def test_routed_experts_full_size_sampled(proj):
             W_hat = G.dequant_weight(br, bsr)
             Cg = host_bits16(c[torch.from_numpy(rows).cuda(), n0:n1])
             check_product(Cg, A_hat @ W_hat.T, A_hat, W_hat, f"{proj} expert {e} block {bi}")
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+@pytest.mark.parametrize("K", [512, 560])
+def test_tile_plan_and_id_mapping_agree(fmt, K):
+    """With a 16-byte aligned workspace the merged grouped launch reads every
+    workgroup's tile from the plan written ahead of it; with a workspace that
+    is only 4-byte aligned each workgroup maps its id to its tile itself.  The
+    two must give the same bytes, for the plain, the gated and the gathered
+    gated product, on experts of every tile height (64-, 128- and 256-row
+    classes, a large expert's remainder tiles, empty experts) and with a
+    partial last K-block."""
+    dev = "cuda"
+    counts = np.array([0, 3, 64, 65, 128, 129, 300, 0, 520, 37, 700, 1, 256, 384])
+    E, M = len(counts), int(counts.sum())
+    N, F = 640, 256
+    kb = lambda n: (n + 127) // 128
+    off = torch.from_numpy(np.r_[0, np.cumsum(counts)].astype(np.int32)).to(dev)
+    x = I.device_normal((M, K), seed=91, std=1.0, device=dev, dtype=torch.bfloat16)
+    a, a_s = ds.act_quant(x, fmt)
+    w = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    w_s = torch.empty((E, kb(N), kb(K)), dtype=torch.float32, device=dev)
+    w13 = torch.empty((E, 2 * F, K), dtype=torch.uint8, device=dev)
+    w13_s = torch.empty((E, kb(2 * F), kb(K)), dtype=torch.float32, device=dev)
+    for e in range(E):
+        q, s = ds.weight_quant(I.device_normal((N, K), seed=500 + e, std=0.02, device=dev), fmt)
+        w[e].copy_(q)
+        w_s[e].copy_(s)
+        q, s = ds.weight_quant(I.device_normal((2 * F, K), seed=700 + e, std=0.02, device=dev), fmt)
+        w13[e].copy_(q)
+        w13_s[e].copy_(s)
+    rows = torch.from_numpy(np.random.default_rng(5).integers(0, M, M).astype(np.int32)).to(dev)
+    lib = ds._lib.load()
+    need = max(lib.dsfp8_grouped_gemm_workspace_bytes(E, M, N, K), lib.dsfp8_grouped_gemm_workspace_bytes(E, M, 2 * F, K))
+    big = torch.empty(need + 64, dtype=torch.uint8, device=dev)
+    planned, unplanned = big[:need], big[4:4 + need]
+    assert planned.data_ptr() % 16 == 0 and unplanned.data_ptr() % 16 == 4
+
+    def outputs(ws):
+        c = ds.grouped_gemm(a, a_s, w, w_s, off, workspace=ws, scale_fmt=fmt)
+        g = ds.grouped_gemm_silu_mul_act_quant(a, a_s, w13, w13_s, off, fmt, return_h=True, workspace=ws)
+        r = ds.grouped_gemm_silu_mul_act_quant(a, a_s, w13, w13_s, off, fmt, return_h=True, workspace=ws, rows=rows)
+        torch.cuda.synchronize()
+        return [t.contiguous().view(torch.uint8).cpu() for t in (c, *g, *r)]
+
+    for name, p, q in zip(["plain", "y", "s", "h", "gathered y", "gathered s", "gathered h"], outputs(planned),
+                          outputs(unplanned)):
+        assert torch.equal(p, q), f"{name}: tile plan and per-workgroup mapping differ"
