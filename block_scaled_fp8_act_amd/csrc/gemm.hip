@@ -2311,6 +2311,7 @@ hipError_t grouped_classes(const GemmArgs& a, hipStream_t stream) {
   GemmArgs c0 = s;
   c0.grp_class = 0;
   const int64_t n = merged_workgroups(a.E, a.M, GLU ? a.glu_f / BK : (a.N + C2::BN - 1) / C2::BN);
+  if (n > INT32_MAX) return hipErrorInvalidConfiguration;  // more workgroups than one launch takes
   const dim3 grid((unsigned)n), blk(C2::kThreads);
   const bool kfull = a.K % BK == 0;
   const int64_t pct = tall_span_pct(a.K);
