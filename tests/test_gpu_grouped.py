@@ -205,3 +205,25 @@ def test_tile_plan_and_id_mapping_agree(fmt, K):
     for name, p, q in zip(["plain", "y", "s", "h", "gathered y", "gathered s", "gathered h"], outputs(planned),
                           outputs(unplanned)):
         assert torch.equal(p, q), f"{name}: tile plan and per-workgroup mapping differ"
+
+
+def test_k_zero_writes_zeros():
+    """K = 0: every row of every expert, in all three tile classes, is an
+    empty sum; the plain product writes zeros over a sentinel, the gated one
+    h = 0, zero codes and the floor scale 1e-4 / 448."""
+    dev = "cuda"
+    counts = np.array([0, 7, 100, 300, 0, 64])
+    E, M, N, F = len(counts), int(counts.sum()), 384, 256
+    off = torch.from_numpy(np.r_[0, np.cumsum(counts)].astype(np.int32)).to(dev)
+    a = torch.empty((M, 0), dtype=torch.uint8, device=dev)
+    a_s = torch.empty((M, 0), dtype=torch.float32, device=dev)
+    c = torch.full((M, N), 0x7fff, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    out = ds.grouped_gemm(a, a_s, torch.empty((E, N, 0), dtype=torch.uint8, device=dev),
+                          torch.empty((E, (N + 127) // 128, 0), dtype=torch.float32, device=dev), off, out=c)
+    y, s, h = ds.grouped_gemm_silu_mul_act_quant(a, a_s, torch.empty((E, 2 * F, 0), dtype=torch.uint8, device=dev),
+                                                 torch.empty((E, 2 * F // 128, 0), dtype=torch.float32, device=dev),
+                                                 off, return_h=True)
+    torch.cuda.synchronize()
+    assert torch.all(out.view(torch.int16) == 0)
+    assert torch.all(y == 0) and torch.all(h.view(torch.int16) == 0)
+    assert np.all(s.cpu().numpy() == np.float32(np.float32(1e-4) / np.float32(448.0)))
