@@ -2268,16 +2268,17 @@ constexpr int kGrpH0 = 64, kGrpH1 = 128, kGrpH2 = 256;
 // Workgroups of a merged grouped launch over E experts, M rows and tn column
 // tiles (a bound: the tile counts are on the device).  A non-empty expert has
 // at most one tile of class 0 or 1 (its only tile, or the remainder after its
-// whole 256-row tiles), so classes 0 and 1 together have at most min(E, M);
-// the large class at most M/256 whole tiles plus one padded tile per expert
-// with more than 128 rows.  Ids go in chunks of 8: each class rounds its
-// tiles up to whole chunks, which classes 0 and 1 together take at most one
-// chunk more than their joint bound.  The kernel maps chunks to the actual
-// tiles and the rest exit.
+// whole 256-row tiles), so classes 0 and 1 together have at most min(E, M).
+// The large class's tiles hold at least 129 rows each on average: a whole
+// tile 256, an expert of 129 to 256 rows one tile, and an expert whose
+// remainder exceeds 128 rows spreads its rows over whole tiles plus one, at
+// more than 128 rows per tile; so it has at most M/129 tiles.  Ids go in
+// chunks of 8: each class rounds its tiles up to whole chunks, which classes
+// 0 and 1 together take at most one chunk more than their joint bound.  The
+// kernel maps chunks to the actual tiles and the rest exit.
 int64_t merged_workgroups(int64_t E, int64_t M, int64_t tn) {
-  auto mn = [](int64_t x, int64_t y) { return x < y ? x : y; };
-  const int64_t s01 = mn(E, M);
-  const int64_t s2 = (M + kGrpH2 - 1) / kGrpH2 + mn(E, M / (kGrpH1 + 1));
+  const int64_t s01 = E < M ? E : M;
+  const int64_t s2 = M / (kGrpH1 + 1);
   return ((s01 * tn + 7) / 8 + 1 + (s2 * tn + 7) / 8) * 8;
 }
 
