@@ -81,9 +81,9 @@ class Timer:
 
 # ---- dense FFN step ---------------------------------------------------------------------
 
-def setup_dense(dev, fmt="fp32", unfused=False):
+def setup_dense(dev, fmt="fp32", unfused=False, inter=None):
     d = I.WORKLOADS["dense_ffn"].dims
-    M, D, F = d["M"], d["dim"], d["inter"]
+    M, D, F = d["M"], d["dim"], inter if inter is not None else d["inter"]
     x = I.device_normal((M, D), seed=301, std=1.0, device=dev, dtype=torch.bfloat16)
     w13 = I.device_normal((2 * F, D), seed=302, std=0.02, device=dev)
     q13, s13 = ds.weight_quant(w13, fmt)
@@ -267,6 +267,29 @@ def bench_dense_unfused(dev, steps):
     M, D, F = st["M"], st["D"], st["F"]
     flop = 2.0 * M * 2 * F * D + 2.0 * M * D * F
     return {"workload": "dense FFN prefill, up-projection, gate and quantisation as separate kernels",
+            "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+            "kernels": dense_kernels(st, T)}
+
+
+def bench_dense_tp_shard(dev, steps, ranks=8):
+    """One rank's share of the dense FFN step under `ranks`-way tensor
+    parallelism, as the pages deploy the model: w1 and w3 split by output
+    rows (column-parallel, [inter/ranks, dim] each), w2 by input columns
+    (row-parallel, [dim, inter/ranks]); every rank quantises the full
+    activations and produces a partial [M, dim] that an all-reduce (not
+    timed here: one GPU) would sum.  Timed as one captured graph per step,
+    like the headline."""
+    F = I.WORKLOADS["dense_ffn"].dims["inter"] // ranks
+    st = setup_dense(dev, inter=F)
+    _, T = run_dense(st, steps, 3)
+    g = capture(lambda: dense_step(st, NoTimer()))
+    b = st["b"]
+    check_replays(g, lambda: dense_step(st, NoTimer()), [b[n] for n in ("xq", "xs", "hq", "hs", "out")])
+    ms = time_graph(g, steps, 3)
+    M, D = st["M"], st["D"]
+    flop = 2.0 * M * 2 * F * D + 2.0 * M * D * F
+    return {"workload": f"dense FFN prefill, one rank of {ranks}-way tensor parallelism: act_quant [{M},{D}] -> "
+                        f"gemm [w1;w3] {M}x{2 * F}x{D} with SiLU gate + act_quant -> gemm w2 {M}x{D}x{F}",
             "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
             "kernels": dense_kernels(st, T)}
 
@@ -661,6 +684,9 @@ def recorded_traffic():
 def only(kernel, reps, dev, fmt="fp32"):
     """Run one kernel of the dense step `reps` times (for counter collection),
     with fp32 or ue8m0 scales throughout."""
+    if kernel == "dense_tp8_rank":
+        print(json.dumps({"only": kernel, "reps": reps, "result": bench_dense_tp_shard(dev, reps)}))
+        return
     if kernel == "routed_experts":
         print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps)}))
         return
@@ -713,7 +739,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["act_quant", "weight_dequant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
-                                       "copy", "routed_experts", "small_products", "grouped_classes"],
+                                       "copy", "routed_experts", "small_products", "grouped_classes", "dense_tp8_rank"],
                     help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
                          "(for rocprofv3)")
     ap.add_argument("--reps", type=int, default=3)
@@ -790,6 +816,8 @@ def main():
         others["dense_ffn_unfused"] = bench_dense_unfused(dev, 20)
         torch.cuda.empty_cache()
         others["dense_ffn_bf16_path"] = bench_bf16_path(dev, 10)
+        torch.cuda.empty_cache()
+        others["dense_ffn_tp8_rank"] = bench_dense_tp_shard(dev, 20)
         torch.cuda.empty_cache()
         others["routed_experts"] = bench_moe(dev, 10)
         others["weight_dequant"] = bench_dequant(dev, 20)

@@ -112,7 +112,8 @@ struct GemmArgs {
   // epilogue computes h = bf16(SiLU(bf16(x w1^T)) * bf16(x w3^T)) and writes
   // act_quant(h) as e4m3 qy [M, F] and fp32 scales qs (element (m, b) at
   // qs[m * qs_rs + b * qs_ks]), and h itself to qh when that is not null.
-  int64_t glu_f;  // F (0: plain product into C)
+  int64_t glu_f;   // F (0: plain product into C)
+  int64_t glu_nt;  // output column blocks of 128 this launch computes (0: all F / 128)
   uint8_t* qy;
   int64_t ldqy;
   float* qs;

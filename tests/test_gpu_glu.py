@@ -193,11 +193,17 @@ def test_integer_operands_exact(M, F_, K, fmt):
 
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
 @pytest.mark.parametrize("M,F_,K", [(1, 128, 256), (64, 256, 7168), (65, 384, 640), (200, 256, 720),
-                                    (1300, 5504, 256), (1300, 5504, 720)])
+                                    (1300, 5504, 256), (1300, 5504, 720), (300, 16640, 720),
+                                    (2048, 5248, 256)])
 def test_random_operands_against_oracle(M, F_, K, fmt):
     # (1300, 5504): 6 x 43 = 258 tiles of 256 x 256, the persistent kernel
     # (two workgroups take a second tile), with M and N tails; K = 720 ends
-    # in a partial K-block
+    # in a partial K-block.  On a 256-CU part the launch splits the output
+    # columns when the 256-row tiles leave a partial round: (300, 16640)
+    # has 2 x 130 tiles, so 128 column blocks run persistent and the last 2
+    # as 64-row tiles (with a row tail); (2048, 5248) has 8 x 41 tiles, so
+    # 32 blocks run persistent and the last 9 as 128-row tiles (9 x 32
+    # 64-row tiles would exceed one round).
     ue = fmt == "ue8m0"
     a, a_s, w, w_s = rand_operands(M, F_, K, ue8m0=ue, seed=M)
     y, s, h, dev = run_dense(a, a_s, w[0], w_s[0], fmt)
@@ -242,12 +248,15 @@ def test_unsupported_layout_raises():
 
 
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
-def test_dense_ffn_full_size_sampled(fmt):
-    """The dense feed-forward up-projection (4096 x 2*18432 x 7168) with
+@pytest.mark.parametrize("F_", [18432, 2304])
+def test_dense_ffn_full_size_sampled(F_, fmt):
+    """The dense feed-forward up-projection (4096 x 2*18432 x 7168), and one
+    rank's share of it under 8-way tensor parallelism (F = 2304: 288 tiles of
+    256 x 256, whose launch splits the output columns on a 256-CU part), with
     device-drawn inputs: bit-identical to the unfused path everywhere, and
     against the oracle on sampled rows and output blocks, with fp32 and with
     power-of-two (ue8m0) scales."""
-    M, K, F_ = 4096, 7168, 18432
+    M, K = 4096, 7168
     ue = fmt == "ue8m0"
     xf = I.device_normal((M, K), seed=80, std=1.0, device="cuda", dtype=torch.bfloat16)
     wf = I.device_normal((2 * F_, K), seed=81, std=0.02, device="cuda")
