@@ -304,18 +304,27 @@ def aq_bytes(M, K, inputs=1):
 
 # ---- other workloads ----------------------------------------------------------------------
 
-def bench_moe(dev, iters):
+def bench_moe(dev, iters, ranks=1):
     """The routed-expert step on the device: routing of the gate's top-k
     choice, act_quant of the routed rows (gathered in the kernel), the grouped
     [w1;w3] product with the SiLU gate and act_quant in its epilogue, the
-    grouped w2 product and the weighted bf16 combine into the token outputs."""
+    grouped w2 product and the weighted bf16 combine into the token outputs.
+
+    ranks > 1: one rank's share under expert parallelism with the experts
+    assigned to ranks contiguously (rank 0 holds the first 256 / ranks): the
+    same routing draw over all experts, routed with the local expert count,
+    so pairs that chose another rank's expert get no row and are skipped by
+    the combine (the all-reduce of the per-rank outputs is not timed: one
+    GPU)."""
     d = I.WORKLOADS["moe"].dims
-    E, D, F, Tk, k = d["experts"], d["dim"], d["inter"], d["tokens"], d["topk"]
-    idx_h, w_h = I.zipf_topk(Tk, E, k, d["zipf_s"])
+    E_all, D, F, Tk, k = d["experts"], d["dim"], d["inter"], d["tokens"], d["topk"]
+    E = E_all // ranks
+    idx_h, w_h = I.zipf_topk(Tk, E_all, k, d["zipf_s"])
     idx = torch.from_numpy(idx_h).to(dev)
     wts = torch.from_numpy(w_h.view(np.int16)).to(dev).view(torch.bfloat16)
-    counts = np.bincount(idx_h.ravel(), minlength=E)
-    M = Tk * k
+    counts = np.bincount(idx_h.ravel(), minlength=E_all)[:E]
+    M = Tk * k            # row buffers: at most every pair
+    rows = int(counts.sum())  # rows routed to this rank's experts
     x = I.device_normal((Tk, D), seed=401, std=1.0, device=dev, dtype=torch.bfloat16)
     q13 = torch.empty((E, 2 * F, D), dtype=torch.uint8, device=dev)
     s13 = torch.empty((E, kb(2 * F), kb(D)), dtype=torch.float32, device=dev)
@@ -333,14 +342,15 @@ def bench_moe(dev, iters):
     del w, q, s
     lib = ds._lib.load()
     offd = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    row_token = torch.empty(M, dtype=torch.int32, device=dev)
+    row_token = torch.zeros(M, dtype=torch.int32, device=dev)
     token_rows = torch.empty((Tk, k), dtype=torch.int32, device=dev)
     rws = torch.empty(lib.dsfp8_moe_route_workspace_bytes(Tk, k, E), dtype=torch.uint8, device=dev)
     xq = torch.empty((Tk, D), dtype=torch.uint8, device=dev)
     xs = ds.new_scales(Tk, kb(D), dev)
-    hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
-    hs = ds.new_scales(M, kb(F), dev)
-    yr = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    # zero-filled: with ranks > 1 the rows past this rank's are never written
+    hq = torch.zeros((M, F), dtype=torch.uint8, device=dev)
+    hs = ds.new_scales(M, kb(F), dev).zero_()
+    yr = torch.zeros((M, D), dtype=torch.bfloat16, device=dev)
     y = torch.empty((Tk, D), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(lib.dsfp8_grouped_gemm_workspace_bytes(E, M, D, D), dtype=torch.uint8, device=dev)
     T = Timer()
@@ -375,10 +385,14 @@ def bench_moe(dev, iters):
     s1.record()
     T.collect()
     torch.cuda.synchronize()
-    flop_up, flop_dn = 2.0 * M * 2 * F * D, 2.0 * M * D * F
-    by_up = M * D + E * 2 * F * D + 4 * (M * kb(D) + E * kb(2 * F) * kb(D)) + M * F + 4 * M * kb(F)
-    by_dn = M * F + E * D * F + 4 * (M * kb(F) + E * kb(D) * kb(F)) + 2 * M * D
-    res = {"workload": I.WORKLOADS["moe"].desc, "rows": M,
+    R = rows
+    flop_up, flop_dn = 2.0 * R * 2 * F * D, 2.0 * R * D * F
+    by_up = R * D + E * 2 * F * D + 4 * (R * kb(D) + E * kb(2 * F) * kb(D)) + R * F + 4 * R * kb(F)
+    by_dn = R * F + E * D * F + 4 * (R * kb(F) + E * kb(D) * kb(F)) + 2 * R * D
+    desc = I.WORKLOADS["moe"].desc
+    if ranks > 1:
+        desc += f"; one rank of {ranks}-way expert parallelism ({E} local experts)"
+    res = {"workload": desc, "rows": R,
            "expert_rows": {"min": int(counts.min()), "median": float(np.median(counts)),
                            "max": int(counts.max())}}
     for name, fl, by in (("grouped_up_gate", flop_up, by_up), ("grouped_down", flop_dn, by_dn)):
@@ -388,7 +402,7 @@ def bench_moe(dev, iters):
                      "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3)}
     # act_quant reads the token rows of x (2 B), writes e4m3 and scales;
     # combine reads the expert outputs and writes the token outputs (bf16).
-    for name, by in (("act_quant", aq_bytes(Tk, D)), ("combine", 2 * M * D + 2 * Tk * D + Tk * k * 10)):
+    for name, by in (("act_quant", aq_bytes(Tk, D)), ("combine", 2 * R * D + 2 * Tk * D + Tk * k * 10)):
         us = T.avg_us(name)
         res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
                      "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
@@ -690,6 +704,9 @@ def only(kernel, reps, dev, fmt="fp32"):
     if kernel == "routed_experts":
         print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps)}))
         return
+    if kernel == "routed_experts_ep8_rank":
+        print(json.dumps({"only": kernel, "reps": reps, "result": bench_moe(dev, reps, ranks=8)}))
+        return
     if kernel == "grouped_classes":
         print(json.dumps({"only": kernel, "reps": reps, "result": bench_grouped_classes(dev, reps)}))
         return
@@ -739,7 +756,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline step only (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["act_quant", "weight_dequant", "gemm_up_gate", "gemm_up", "silu_mul_act_quant", "gemm_down",
-                                       "copy", "routed_experts", "small_products", "grouped_classes", "dense_tp8_rank"],
+                                       "copy", "routed_experts", "small_products", "grouped_classes", "dense_tp8_rank",
+                                       "routed_experts_ep8_rank"],
                     help="run one kernel of the dense step (or the routed-expert step) --reps times and exit "
                          "(for rocprofv3)")
     ap.add_argument("--reps", type=int, default=3)
@@ -820,6 +838,7 @@ def main():
         others["dense_ffn_tp8_rank"] = bench_dense_tp_shard(dev, 20)
         torch.cuda.empty_cache()
         others["routed_experts"] = bench_moe(dev, 10)
+        others["routed_experts_ep8_rank"] = bench_moe(dev, 10, ranks=8)
         others["weight_dequant"] = bench_dequant(dev, 20)
         others["decode_qa"] = bench_small_gemm(dev, 50, "decode MLA q_a: 32x1536x7168", 32, 1536, 7168, "fp32", True)
         others["ragged_ue8m0"] = bench_small_gemm(dev, 50, "ragged ue8m0: 333x2500x1000", 333, 2500, 1000,
