@@ -106,7 +106,7 @@ def test_act_quant_rows_clamps_indices():
 
 
 @pytest.mark.parametrize("T,E,k,D", [(512, 64, 8, 7168), (200, 16, 2, 300), (33, 40, 16, 136), (64, 8, 1, 64),
-                                     (100, 32, 6, 1000)])
+                                     (100, 32, 6, 1000), (50, 16, 4, 3004), (40, 64, 8, 2056)])
 def test_combine(T, E, k, D):
     idx, w = I.zipf_topk(T, E, k, 1.1, seed=D)
     _, _, _, tr = moe.route(idx, E)
@@ -133,6 +133,28 @@ def test_combine_skips_pairs_without_row():
         kk = np.nonzero(keep[t])[0]
         ref[t] = moe.combine(yr, w[t:t + 1, kk], idx[t:t + 1, kk], tr[t:t + 1, kk])[0]
     assert np.array_equal(host_bits16(out), ref)
+
+
+def test_combine_one_rank_of_experts():
+    """The pairs routed to other ranks' experts get no row (routing with the
+    local expert count), as in one rank's share under expert parallelism:
+    each token combines only its local pairs, bit for bit the oracle's
+    combine over those pairs."""
+    T, E, k, D, El = 300, 64, 8, 7168, 8
+    idx, w = I.zipf_topk(T, E, k, 1.1, seed=12)
+    _, _, _, tr = moe.route(idx, El)
+    R = int((tr >= 0).sum())
+    yr = I.activations((max(R, 1), D), I.MOE, 45, std=3.0)
+    out = ds.moe_combine(dev_bf16(yr), dev_i32(idx), dev_bf16(w), dev_i32(tr))
+    torch.cuda.synchronize()
+    got = host_bits16(out)
+    for t in range(T):
+        kk = np.nonzero(tr[t] >= 0)[0]
+        if len(kk) == 0:
+            assert np.all(got[t] == 0), f"token {t} without local pairs"
+            continue
+        ref = moe.combine(yr, w[t:t + 1, kk], idx[t:t + 1, kk], tr[t:t + 1, kk])[0]
+        assert np.array_equal(got[t], ref), f"token {t}"
 
 
 # Accumulation term of the products' element-wise bound, relative to
