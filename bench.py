@@ -273,9 +273,10 @@ def bench_dense_unfused(dev, steps):
 
 def bench_dense_tp_shard(dev, steps, ranks=8):
     """One rank's share of the dense FFN step under `ranks`-way tensor
-    parallelism, as the pages deploy the model: w1 and w3 split by output
-    rows (column-parallel, [inter/ranks, dim] each), w2 by input columns
-    (row-parallel, [dim, inter/ranks]); every rank quantises the full
+    parallelism ("DeepSeek-V3 Administrator & Developer Guide" 1.2, the
+    column- and row-parallel linears, and 5.3, multi-GPU tensor-parallel
+    inference): w1 and w3 split by output rows ([inter/ranks, dim] each),
+    w2 by input columns ([dim, inter/ranks]); every rank quantises the full
     activations and produces a partial [M, dim] that an all-reduce (not
     timed here: one GPU) would sum.  Timed as one captured graph per step,
     like the headline."""
@@ -311,7 +312,9 @@ def bench_moe(dev, iters, ranks=1):
     grouped w2 product and the weighted bf16 combine into the token outputs.
 
     ranks > 1: one rank's share under expert parallelism with the experts
-    assigned to ranks contiguously (rank 0 holds the first 256 / ranks): the
+    assigned to ranks contiguously, as the checkpoint conversion shards them
+    by expert index ("DeepSeek-V3 Administrator & Developer Guide" 1.1;
+    rank 0 holds the first 256 / ranks): the
     same routing draw over all experts, routed with the local expert count,
     so pairs that chose another rank's expert get no row and are skipped by
     the combine (the all-reduce of the per-rank outputs is not timed: one
