@@ -103,6 +103,49 @@ def test_single_expert_equals_dense():
     assert np.array_equal(C, host_bits16(Cd))
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_rows_past_the_last_expert(fmt):
+    """Row buffers sized for more rows than the experts own (one rank's share
+    under expert parallelism: sized for every routed pair, only the local
+    experts' rows counted by the offsets): the owned rows are bit for bit
+    the product over exactly those rows, and the rows past offsets[E] are
+    left as they were, for the plain and the gated-and-gathered forms."""
+    ue = fmt == "ue8m0"
+    counts = [5, 0, 300, 70, 129, 1]
+    a, a_s, b, b_s, off = _case(counts, 256, 384, 31, ue8m0=ue)
+    R = int(off[-1])
+    extra = 700
+    g = np.random.default_rng(31)
+    a_big = np.concatenate([a, g.integers(0, 126, (extra, a.shape[1])).astype(np.uint8)])
+    as_big = np.concatenate([a_s, np.full((extra, a_s.shape[1]), 0.5, np.float32)])
+    offd = torch.from_numpy(off).cuda()
+    sentinel = 0x3F80  # bf16 1.0
+    c = torch.full((R + extra, 256), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ds.grouped_gemm(dev_u8(a_big), dev_scales(as_big, "kb"), dev_u8(b), dev_f32(b_s), offd, out=c, scale_fmt=fmt)
+    want = _run(a, a_s, b, b_s, off, scale_fmt=fmt)
+    got = host_bits16(c)
+    assert np.array_equal(got[:R], want), "owned rows differ from the product over exactly those rows"
+    assert np.all(got[R:] == sentinel), "rows past the last expert were written"
+
+    # gated form, rows read through an index as in the routed step
+    F_ = 128
+    q13 = np.stack([Q.weight_quant(I.weights_f32((2 * F_, 384), I.MOE, 77 + e), ue8m0=ue)[0]
+                    for e in range(len(counts))])
+    s13 = np.stack([Q.weight_quant(I.weights_f32((2 * F_, 384), I.MOE, 77 + e), ue8m0=ue)[1]
+                    for e in range(len(counts))])
+    src = g.permutation(R + extra).astype(np.int32)  # product row r reads row src[r] of a_big
+    rows_big = torch.from_numpy(src).cuda()
+    y = torch.full((R + extra, F_), 0x5A, dtype=torch.uint8, device="cuda")
+    sc = ds.new_scales(R + extra, 1, "cuda").fill_(-1.0)
+    ds.grouped_gemm_silu_mul_act_quant(dev_u8(a_big), dev_scales(as_big, "kb"), dev_u8(q13), dev_f32(s13), offd, fmt,
+                                       out=(y, sc), rows=rows_big)
+    y_ref, s_ref = ds.grouped_gemm_silu_mul_act_quant(dev_u8(a_big), dev_scales(as_big, "kb"), dev_u8(q13),
+                                                      dev_f32(s13), offd, fmt, rows=rows_big[:R].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y[:R], y_ref) and torch.equal(sc[:R].contiguous(), s_ref.contiguous()), "gated owned rows"
+    assert torch.all(y[R:] == 0x5A) and torch.all(sc[R:] == -1.0), "gated rows past the last expert were written"
+
+
 def test_all_rows_in_last_expert():
     a, a_s, b, b_s, off = _case([0, 0, 0, 200], 128, 384, 4)
     C = _run(a, a_s, b, b_s, off)
