@@ -74,6 +74,11 @@ class Timer:
     def avg_us(self, name):
         return float(np.mean(self.samples[name]))
 
+    def spread(self, name):
+        """Median and minimum of a kernel's launches (us), beside the mean."""
+        v = self.samples[name]
+        return {"us_median": round(float(np.median(v)), 1), "us_min": round(float(np.min(v)), 1), "launches": len(v)}
+
     def reset(self):
         self.samples = {}
         self.pending = []
@@ -193,14 +198,14 @@ def dense_kernels(st, T):
         us = T.avg_us(name)
         k[name] = {"shape": [M, 2 * F if name == up else D, D if name == up else F],
                    "us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
-                   "frac_of_fp8_peak": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+                   "frac_of_fp8_peak": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4), **T.spread(name)}
     mem = [("act_quant", aq_bytes(M, D))]
     if st["unfused"]:
         mem.append(("silu_mul_act_quant", aq_bytes(M, F, 2)))
     for name, by in mem:
         us = T.avg_us(name)
         k[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
-                   "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}
+                   "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4), **T.spread(name)}
     return k
 
 
@@ -402,14 +407,14 @@ def bench_moe(dev, iters, ranks=1):
         us = T.avg_us(name)
         roof_us = max(fl / (PEAK_FP8_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)) * 1e6
         res[name] = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
-                     "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3)}
+                     "roofline_us": round(roof_us, 1), "frac_of_roofline": round(roof_us / us, 3), **T.spread(name)}
     # act_quant reads the token rows of x (2 B), writes e4m3 and scales;
     # combine reads the expert outputs and writes the token outputs (bf16).
     for name, by in (("act_quant", aq_bytes(Tk, D)), ("combine", 2 * R * D + 2 * Tk * D + Tk * k * 10)):
         us = T.avg_us(name)
         res[name] = {"us": round(us, 1), "gbs": round(by / us / 1e3, 1),
-                     "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3)}
-    res["route"] = {"us": round(T.avg_us("route"), 1)}
+                     "frac_of_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 3), **T.spread(name)}
+    res["route"] = {"us": round(T.avg_us("route"), 1), **T.spread("route")}
     res["step_us_eager"] = round(s0.elapsed_time(s1) * 1e3 / iters, 1)
     g = capture(lambda: step(NoTimer()))
     check_replays(g, lambda: step(NoTimer()), [offd, row_token, token_rows, xq, xs, hq, hs, yr, y])
